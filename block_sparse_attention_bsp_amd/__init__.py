@@ -1,0 +1,231 @@
+"""Dynamic block-sparse causal prefill attention for AMD MI355X (gfx950).
+
+Python binding of ``libbsp.so`` (include/bsp.h).  This module only marshals
+arguments: torch provides device memory and the current stream, and every
+step of the computation runs in the library's HIP kernels.  There is no CPU
+or PyTorch fallback: if the library is missing, loading fails loudly.
+
+Three stages, as on the FlashPrefill summary page (paperlayer.ai, Appendix B):
+``score`` (pool + block scores), ``mask`` (max-based dynamic threshold +
+index compaction) and ``attn_fwd`` (block-sparse online-softmax attention);
+``prefill`` chains them.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+import torch
+
+__all__ = [
+    "BspError", "BspDesc", "lib", "library_path", "desc", "score", "mask", "attn_fwd", "prefill",
+    "bsp_score", "bsp_mask", "bsp_attn_fwd", "bsp_status_string", "bsp_abi_version",
+    "DTYPE_F32", "DTYPE_BF16", "DTYPE_FP8_E4M3",
+]
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+library_path = os.path.join(_PKG, "libbsp.so")
+
+DTYPE_F32, DTYPE_BF16, DTYPE_FP8_E4M3 = 0, 1, 2
+_STATUS = {0: "BSP_OK", 1: "BSP_ERR_NULL_POINTER", 2: "BSP_ERR_BAD_SHAPE", 3: "BSP_ERR_BAD_DTYPE",
+           4: "BSP_ERR_BAD_VALUE", 5: "BSP_ERR_UNSUPPORTED", 6: "BSP_ERR_HIP"}
+
+
+class BspDesc(ctypes.Structure):
+    """Mirror of ``bsp_desc`` in include/bsp.h."""
+    _fields_ = [
+        ("hq", ctypes.c_int32), ("hkv", ctypes.c_int32), ("seq", ctypes.c_int32),
+        ("d", ctypes.c_int32), ("block", ctypes.c_int32), ("gamma", ctypes.c_float),
+        ("sm_scale", ctypes.c_float), ("causal", ctypes.c_int32),
+        ("sink_blocks", ctypes.c_int32), ("local_blocks", ctypes.c_int32),
+        ("dtype", ctypes.c_int32), ("q_scale", ctypes.c_void_p), ("k_scale", ctypes.c_void_p),
+        ("v_scale", ctypes.c_void_p),
+    ]
+
+
+class BspError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"{_STATUS.get(status, status)}: {message}")
+        self.status = status
+
+
+_lib = None
+
+
+def lib():
+    """Load libbsp.so (built in-tree by block_sparse_attention_bsp_amd.build)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(library_path):
+            raise RuntimeError(f"{library_path} is not built; run "
+                               "`python -m block_sparse_attention_bsp_amd.build`")
+        L = ctypes.CDLL(library_path)
+        vp, P = ctypes.c_void_p, ctypes.POINTER(BspDesc)
+        L.bsp_score.argtypes = [P, vp, vp, vp, vp, vp, vp]
+        L.bsp_mask.argtypes = [P, vp, vp, vp, vp, vp, vp]
+        L.bsp_attn_fwd.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp]
+        for f in (L.bsp_score, L.bsp_mask, L.bsp_attn_fwd):
+            f.restype = ctypes.c_int32
+        L.bsp_status_string.argtypes = [ctypes.c_int32]
+        L.bsp_status_string.restype = ctypes.c_char_p
+        L.bsp_abi_version.restype = ctypes.c_int32
+        _lib = L
+    return _lib
+
+
+# ---------------------------------------------------------------- raw C ABI
+def bsp_status_string(status: int) -> str:
+    return lib().bsp_status_string(status).decode()
+
+
+def bsp_abi_version() -> int:
+    return int(lib().bsp_abi_version())
+
+
+def _check(status: int):
+    if status != 0:
+        raise BspError(status, bsp_status_string(status))
+
+
+def bsp_score(d: BspDesc, q, k, q_pool, k_pool, score_out, stream) -> int:
+    return lib().bsp_score(ctypes.byref(d), q, k, q_pool, k_pool, score_out, stream)
+
+
+def bsp_mask(d: BspDesc, score_in, user_mask, mask_out, kv_idx, kv_cnt, stream) -> int:
+    return lib().bsp_mask(ctypes.byref(d), score_in, user_mask, mask_out, kv_idx, kv_cnt, stream)
+
+
+def bsp_attn_fwd(d: BspDesc, q, k, v, kv_idx, kv_cnt, o, lse, stream) -> int:
+    return lib().bsp_attn_fwd(ctypes.byref(d), q, k, v, kv_idx, kv_cnt, o, lse, stream)
+
+
+# ---------------------------------------------------------------- torch level
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.float32:
+        return DTYPE_F32
+    if t.dtype == torch.bfloat16:
+        return DTYPE_BF16
+    if t.dtype in (torch.uint8, torch.float8_e4m3fn):
+        return DTYPE_FP8_E4M3
+    raise BspError(3, f"unsupported tensor dtype {t.dtype}")
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    if t is None:
+        return None
+    if t.numel() == 0:
+        return None
+    if not t.is_cuda:
+        raise BspError(1, "tensors must be device tensors")
+    if not t.is_contiguous():
+        raise BspError(2, "tensors must be contiguous")
+    return t.data_ptr()
+
+
+def _stream():
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def desc(hq: int, hkv: int, seq: int, d: int, block: int, dtype: int, gamma: float = 0.0,
+         sm_scale: float = 0.0, sink_blocks: int = 1, local_blocks: int = 1, causal: int = 1,
+         q_scale=None, k_scale=None, v_scale=None) -> BspDesc:
+    return BspDesc(hq, hkv, seq, d, block, gamma, sm_scale, causal, sink_blocks, local_blocks,
+                   dtype, _ptr(q_scale), _ptr(k_scale), _ptr(v_scale))
+
+
+def _shape(t: Optional[torch.Tensor], want, name: str):
+    """Shape checks before the C call: the C ABI sees only pointers, so a
+    tensor smaller than the descriptor says would be read out of bounds."""
+    if t is not None and tuple(t.shape) != tuple(want):
+        raise BspError(2, f"{name} has shape {tuple(t.shape)}, expected {tuple(want)}")
+
+
+def _desc_qkv(q, k, block, v=None, **kw):
+    if q.dim() != 3 or k.dim() != 3:
+        raise BspError(2, "q and k must be [heads, seq, d]")
+    hq, seq, d = q.shape
+    _shape(k, (k.shape[0], seq, d), "k")
+    _shape(v, k.shape, "v")
+    for t in (k, v):
+        if t is not None and t.dtype != q.dtype:
+            raise BspError(3, "q, k and v must share one dtype")
+    for name, want in (("q_scale", hq), ("k_scale", k.shape[0]), ("v_scale", k.shape[0])):
+        t = kw.get(name)
+        _shape(t, (want,), name)
+        if t is not None and t.dtype != torch.float32:
+            raise BspError(3, f"{name} must be float32")
+    return desc(hq, k.shape[0], seq, d, block, _dtype_code(q), **kw)
+
+
+def score(q: torch.Tensor, k: torch.Tensor, block: int, sm_scale: float = 0.0,
+          q_scale=None, k_scale=None):
+    """Stage 1.  Returns (q_pool [hq,nb,d], k_pool [hkv,nb,d], score [hq,nb,nb]) fp32."""
+    dsc = _desc_qkv(q, k, block, sm_scale=sm_scale, q_scale=q_scale, k_scale=k_scale)
+    hq, seq, d = q.shape
+    nb = -(-seq // block)
+    qp = torch.empty((hq, nb, d), dtype=torch.float32, device=q.device)
+    kp = torch.empty((k.shape[0], nb, d), dtype=torch.float32, device=q.device)
+    sc = torch.empty((hq, nb, nb), dtype=torch.float32, device=q.device)
+    _check(bsp_score(dsc, _ptr(q), _ptr(k), _ptr(qp), _ptr(kp), _ptr(sc), _stream()))
+    return qp, kp, sc
+
+
+def mask(score_t: Optional[torch.Tensor], gamma: float, seq: int, block: int,
+         sink_blocks: int = 1, local_blocks: int = 1, user_mask: Optional[torch.Tensor] = None,
+         want_mask: bool = True):
+    """Stage 2.  Returns (mask uint8 or None, kv_idx int32 [hq,nb,nb], kv_cnt int32 [hq,nb])."""
+    ref = score_t if score_t is not None else user_mask
+    hq, nb, _ = ref.shape
+    if nb != -(-seq // block):
+        raise BspError(2, "score / user_mask do not match seq and block")
+    _shape(score_t, (hq, nb, nb), "score")
+    _shape(user_mask, (hq, nb, nb), "user_mask")
+    if score_t is not None and score_t.dtype != torch.float32:
+        raise BspError(3, "score must be float32")
+    if user_mask is not None and user_mask.dtype not in (torch.uint8, torch.bool):
+        raise BspError(3, "user_mask must be uint8")
+    dsc = desc(hq, 1, seq, 64, block, DTYPE_F32, gamma=gamma, sink_blocks=sink_blocks,
+               local_blocks=local_blocks)
+    m = torch.empty((hq, nb, nb), dtype=torch.uint8, device=ref.device) if want_mask else None
+    idx = torch.empty((hq, nb, nb), dtype=torch.int32, device=ref.device)
+    cnt = torch.empty((hq, nb), dtype=torch.int32, device=ref.device)
+    _check(bsp_mask(dsc, _ptr(score_t), _ptr(user_mask), _ptr(m), _ptr(idx), _ptr(cnt), _stream()))
+    return m, idx, cnt
+
+
+def attn_fwd(q, k, v, block: int, kv_idx=None, kv_cnt=None, sm_scale: float = 0.0,
+             q_scale=None, k_scale=None, v_scale=None, want_lse: bool = True, out=None, lse=None):
+    """Stage 3.  Returns (o [hq,seq,d] fp32 for fp32 input else bf16, lse [hq,seq] fp32)."""
+    dsc = _desc_qkv(q, k, block, v=v, sm_scale=sm_scale, q_scale=q_scale, k_scale=k_scale,
+                    v_scale=v_scale)
+    hq, seq, d = q.shape
+    nb = -(-seq // block)
+    _shape(kv_idx, (hq, nb, nb), "kv_idx")
+    _shape(kv_cnt, (hq, nb), "kv_cnt")
+    for t in (kv_idx, kv_cnt):
+        if t is not None and t.dtype != torch.int32:
+            raise BspError(3, "kv_idx / kv_cnt must be int32")
+    odt = torch.float32 if q.dtype == torch.float32 else torch.bfloat16
+    if out is not None and (tuple(out.shape) != (hq, seq, d) or out.dtype != odt):
+        raise BspError(2, "out has the wrong shape or dtype")
+    o = out if out is not None else torch.empty((hq, seq, d), dtype=odt, device=q.device)
+    if lse is None and want_lse:
+        lse = torch.empty((hq, seq), dtype=torch.float32, device=q.device)
+    _shape(lse, (hq, seq), "lse")
+    _check(bsp_attn_fwd(dsc, _ptr(q), _ptr(k), _ptr(v), _ptr(kv_idx), _ptr(kv_cnt), _ptr(o),
+                        _ptr(lse), _stream()))
+    return o, lse
+
+
+def prefill(q, k, v, block: int, gamma: float, sm_scale: float = 0.0, sink_blocks: int = 1,
+            local_blocks: int = 1, user_mask=None, q_scale=None, k_scale=None, v_scale=None):
+    """All three stages on the current stream.  Returns a dict of every output."""
+    out = {}
+    if user_mask is None:
+        out["q_pool"], out["k_pool"], out["score"] = score(q, k, block, sm_scale, q_scale, k_scale)
+    m, idx, cnt = mask(out.get("score"), gamma, q.shape[1], block, sink_blocks, local_blocks,
+                       user_mask=user_mask)
+    o, lse = attn_fwd(q, k, v, block, idx, cnt, sm_scale, q_scale, k_scale, v_scale)
+    out.update(mask=m, kv_idx=idx, kv_cnt=cnt, o=o, lse=lse)
+    return out

@@ -1,0 +1,130 @@
+// C-ABI host layer of libbsp: argument checks on the host, then kernel
+// launches on the caller's stream.  No allocation, no synchronisation, no
+// global state.  The operations are defined in include/bsp.h.
+#include <math.h>
+
+#include "bsp.h"
+#include "internal.h"
+
+namespace {
+
+using bsp::Shape;
+
+bsp_status check_desc(const bsp_desc *d, bool need_dtype) {
+  if (!d) return BSP_ERR_NULL_POINTER;
+  if (d->hq < 1 || d->hq > BSP_MAX_HEADS || d->hkv < 1 || d->hkv > d->hq || d->hq % d->hkv)
+    return BSP_ERR_BAD_SHAPE;
+  if (d->seq < 0 || d->seq > BSP_MAX_SEQ) return BSP_ERR_BAD_SHAPE;
+  if (d->d != 64 && d->d != 128) return BSP_ERR_BAD_SHAPE;
+  if (d->block != 64 && d->block != 128) return BSP_ERR_BAD_SHAPE;
+  if (d->causal != 1) return BSP_ERR_UNSUPPORTED;
+  if (need_dtype) {
+    if (d->dtype != BSP_DTYPE_F32 && d->dtype != BSP_DTYPE_BF16 && d->dtype != BSP_DTYPE_FP8_E4M3)
+      return BSP_ERR_BAD_DTYPE;
+  }
+  if (!isfinite(d->sm_scale)) return BSP_ERR_BAD_VALUE;
+  return BSP_OK;
+}
+
+Shape shape_of(const bsp_desc *d) {
+  Shape s;
+  s.hq = d->hq;
+  s.hkv = d->hkv;
+  s.seq = d->seq;
+  s.d = d->d;
+  s.block = d->block;
+  s.nb = (d->seq + d->block - 1) / d->block;
+  s.dtype = d->dtype;
+  return s;
+}
+
+float scale_of(const bsp_desc *d) {
+  return d->sm_scale > 0.f ? d->sm_scale : 1.0f / sqrtf((float)d->d);
+}
+
+bsp_status hip_status(hipError_t e) { return e == hipSuccess ? BSP_OK : BSP_ERR_HIP; }
+
+}  // namespace
+
+extern "C" {
+
+bsp_status bsp_score(const bsp_desc *desc, const void *q, const void *k, float *q_pool,
+                     float *k_pool, float *score, void *stream) {
+  bsp_status st = check_desc(desc, true);
+  if (st != BSP_OK) return st;
+  if (desc->seq == 0) return BSP_OK;
+  if (!q || !k || !q_pool || !k_pool || !score) return BSP_ERR_NULL_POINTER;
+  const bool fp8 = desc->dtype == BSP_DTYPE_FP8_E4M3;
+  if (fp8 && (!desc->q_scale || !desc->k_scale)) return BSP_ERR_BAD_DTYPE;
+  if (!fp8 && (desc->q_scale || desc->k_scale || desc->v_scale)) return BSP_ERR_BAD_DTYPE;
+  const Shape s = shape_of(desc);
+  hipStream_t hs = (hipStream_t)stream;
+  hipError_t e = bsp::launch_pool(s, q, k, desc->q_scale, desc->k_scale, q_pool, k_pool, hs);
+  if (e != hipSuccess) return BSP_ERR_HIP;
+  return hip_status(bsp::launch_score(s, scale_of(desc), q_pool, k_pool, score, hs));
+}
+
+bsp_status bsp_mask(const bsp_desc *desc, const float *score, const uint8_t *user_mask,
+                    uint8_t *mask, int32_t *kv_idx, int32_t *kv_cnt, void *stream) {
+  bsp_status st = check_desc(desc, false);
+  if (st != BSP_OK) return st;
+  if (!(desc->gamma >= 0.f && desc->gamma <= 1.f)) return BSP_ERR_BAD_VALUE;  // also NaN
+  if (desc->sink_blocks < 0 || desc->local_blocks < 0) return BSP_ERR_BAD_VALUE;
+  if (desc->seq == 0) return BSP_OK;
+  if ((!score && !user_mask) || !kv_idx || !kv_cnt) return BSP_ERR_NULL_POINTER;
+  const Shape s = shape_of(desc);
+  return hip_status(bsp::launch_mask(s, desc->gamma, desc->sink_blocks, desc->local_blocks,
+                                     user_mask ? nullptr : score, user_mask, mask, kv_idx, kv_cnt,
+                                     (hipStream_t)stream));
+}
+
+bsp_status bsp_attn_fwd(const bsp_desc *desc, const void *q, const void *k, const void *v,
+                        const int32_t *kv_idx, const int32_t *kv_cnt, void *o, float *lse,
+                        void *stream) {
+  bsp_status st = check_desc(desc, true);
+  if (st != BSP_OK) return st;
+  if (desc->seq == 0) return BSP_OK;
+  if (!q || !k || !v || !o) return BSP_ERR_NULL_POINTER;
+  if ((kv_idx == nullptr) != (kv_cnt == nullptr)) return BSP_ERR_NULL_POINTER;
+  const bool fp8 = desc->dtype == BSP_DTYPE_FP8_E4M3;
+  if (fp8 && (!desc->q_scale || !desc->k_scale || !desc->v_scale)) return BSP_ERR_BAD_DTYPE;
+  if (!fp8 && (desc->q_scale || desc->k_scale || desc->v_scale)) return BSP_ERR_BAD_DTYPE;
+  const Shape s = shape_of(desc);
+  bsp::AttnArgs a;
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.kv_idx = kv_idx;
+  a.kv_cnt = kv_cnt;
+  a.q_scale = desc->q_scale;
+  a.k_scale = desc->k_scale;
+  a.v_scale = desc->v_scale;
+  a.o = o;
+  a.lse = lse;
+  a.sm_scale = scale_of(desc);
+  hipStream_t hs = (hipStream_t)stream;
+  hipError_t e;
+  switch (desc->dtype) {
+    case BSP_DTYPE_F32: e = bsp::launch_attn_f32(s, a, hs); break;
+    case BSP_DTYPE_BF16: e = bsp::launch_attn_bf16(s, a, hs); break;
+    default: e = bsp::launch_attn_fp8(s, a, hs); break;
+  }
+  return hip_status(e);
+}
+
+const char *bsp_status_string(int32_t status) {
+  switch (status) {
+    case BSP_OK: return "BSP_OK";
+    case BSP_ERR_NULL_POINTER: return "BSP_ERR_NULL_POINTER: a required pointer is NULL";
+    case BSP_ERR_BAD_SHAPE: return "BSP_ERR_BAD_SHAPE: sizes out of range or inconsistent";
+    case BSP_ERR_BAD_DTYPE: return "BSP_ERR_BAD_DTYPE: unknown dtype or fp8 scale mismatch";
+    case BSP_ERR_BAD_VALUE: return "BSP_ERR_BAD_VALUE: gamma, sm_scale or window out of range";
+    case BSP_ERR_UNSUPPORTED: return "BSP_ERR_UNSUPPORTED: request not served by this build";
+    case BSP_ERR_HIP: return "BSP_ERR_HIP: the HIP runtime rejected a launch";
+    default: return "unknown bsp_status";
+  }
+}
+
+int32_t bsp_abi_version(void) { return BSP_ABI_VERSION; }
+
+}  // extern "C"

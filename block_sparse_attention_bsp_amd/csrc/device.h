@@ -1,0 +1,59 @@
+// Device-side helpers shared by the gfx950 kernels of libbsp.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace bsp {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef int32_t i32x8 __attribute__((ext_vector_type(8)));
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+// Storage dtypes (values of bsp_dtype).
+constexpr int kF32 = 0;
+constexpr int kBF16 = 1;
+constexpr int kFP8 = 2;
+
+template <int DT> struct Storage;
+template <> struct Storage<kF32> { static constexpr int bytes = 4; };
+template <> struct Storage<kBF16> { static constexpr int bytes = 2; };
+template <> struct Storage<kFP8> { static constexpr int bytes = 1; };
+
+__device__ __forceinline__ float bf16_bits_to_f32(uint32_t b) {
+  return __uint_as_float(b << 16);
+}
+
+// OCP e4m3fn code -> float, by the format: bias 7, 3 mantissa bits,
+// exponent 0 subnormal; the NaN code never occurs in valid inputs.
+__device__ __forceinline__ float e4m3_to_f32(uint32_t c) {
+  uint32_t s = (c & 0x80u) << 24;
+  uint32_t e = (c >> 3) & 15u, m = c & 7u;
+  float v = e ? __uint_as_float(((e + 120u) << 23) | (m << 20)) : (float)m * 0.001953125f;
+  return __uint_as_float(__float_as_uint(v) | s);
+}
+
+// float -> bfloat16 bits, round to nearest even (finite inputs).
+__device__ __forceinline__ uint32_t f32_to_bf16_bits(float x) {
+  uint32_t u = __float_as_uint(x);
+  return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+}
+
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+  return v;
+}
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
+
+}  // namespace bsp

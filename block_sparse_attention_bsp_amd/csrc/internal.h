@@ -1,0 +1,34 @@
+// Launchers shared between the C-ABI host layer (bsp_api.cpp) and the
+// kernel translation units.  Arguments are validated by the caller.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace bsp {
+
+struct Shape {
+  int hq, hkv, seq, d, block, nb, dtype;
+};
+
+struct AttnArgs {
+  const void *q, *k, *v;
+  const int32_t *kv_idx, *kv_cnt;  // both null = dense causal
+  const float *q_scale, *k_scale, *v_scale;
+  void *o;
+  float *lse;
+  float sm_scale;
+};
+
+hipError_t launch_pool(const Shape &s, const void *q, const void *k, const float *q_scale,
+                       const float *k_scale, float *q_pool, float *k_pool, hipStream_t st);
+hipError_t launch_score(const Shape &s, float c, const float *q_pool, const float *k_pool,
+                        float *score, hipStream_t st);
+hipError_t launch_mask(const Shape &s, float gamma, int sink_blocks, int local_blocks,
+                       const float *score, const uint8_t *user_mask, uint8_t *mask,
+                       int32_t *kv_idx, int32_t *kv_cnt, hipStream_t st);
+hipError_t launch_attn_f32(const Shape &s, const AttnArgs &a, hipStream_t st);
+hipError_t launch_attn_bf16(const Shape &s, const AttnArgs &a, hipStream_t st);
+hipError_t launch_attn_fp8(const Shape &s, const AttnArgs &a, hipStream_t st);
+
+}  // namespace bsp

@@ -1,0 +1,166 @@
+/*
+ * bsp.h - C ABI of the dynamic block-sparse causal prefill attention library
+ * (libbsp.so, HIP kernels for gfx950 / MI355X).
+ *
+ * The method is the three-stage pipeline of the FlashPrefill summary page
+ * (paperlayer.ai, "FlashPrefill: Instantaneous Pattern Discovery and
+ * Thresholding for Ultra-Fast Long-Context Prefilling"): instantaneous
+ * pattern discovery over pooled blocks, max-based dynamic thresholding with
+ * block selection, then block-sparse attention (Appendix B "Detailed
+ * Implementation").  One call per stage:
+ *
+ *   bsp_score     pool Q and K into B-token blocks, score query blocks against
+ *                 causally valid key blocks, normalise each row;
+ *   bsp_mask      keep blocks whose score reaches gamma times the row maximum,
+ *                 OR the sink and local-window blocks, AND causal, and compress
+ *                 each row into an ascending list of key-block indices;
+ *   bsp_attn_fwd  online-softmax attention over the kept key blocks only.
+ *
+ * Conventions shared by every entry point
+ *   - Tensor pointers are DEVICE pointers owned by the caller; the library
+ *     allocates nothing, keeps no global state and never synchronises.
+ *   - Work is enqueued on `stream` (a hipStream_t; NULL = the null stream)
+ *     and completes asynchronously.
+ *   - All checks run on the host before any launch.  On any error status
+ *     nothing is launched and no output is touched.  BSP_ERR_HIP means a
+ *     launch was rejected (hipGetLastError after the launch); faults inside
+ *     a kernel surface at the caller's next synchronisation.
+ *   - Layouts are row-major and contiguous: Q [hq][seq][d], K and V
+ *     [hkv][seq][d].  q head h reads kv head h / (hq / hkv) (GQA).
+ *   - nb = ceil(seq / block).  A last block shorter than `block` holds the
+ *     seq % block tail tokens; it pools over those tokens only.
+ *   - seq == 0 is valid and does nothing (after the descriptor checks; the
+ *     tensor pointers are then not checked and may be NULL).
+ *   - Calls on different streams with disjoint outputs may run concurrently;
+ *     the library is thread-safe.
+ */
+#ifndef BSP_H
+#define BSP_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define BSP_ABI_VERSION 1
+
+typedef enum bsp_status {
+  BSP_OK = 0,
+  BSP_ERR_NULL_POINTER = 1, /* a required pointer is NULL */
+  BSP_ERR_BAD_SHAPE = 2,    /* sizes out of range or inconsistent */
+  BSP_ERR_BAD_DTYPE = 3,    /* unknown dtype, or fp8 scales missing / given for non-fp8 */
+  BSP_ERR_BAD_VALUE = 4,    /* gamma, sm_scale or window sizes out of range */
+  BSP_ERR_UNSUPPORTED = 5,  /* valid request this build does not serve (non-causal) */
+  BSP_ERR_HIP = 6           /* the HIP runtime rejected a launch */
+} bsp_status;
+
+typedef enum bsp_dtype {
+  BSP_DTYPE_F32 = 0,     /* IEEE binary32 */
+  BSP_DTYPE_BF16 = 1,    /* bfloat16 */
+  BSP_DTYPE_FP8_E4M3 = 2 /* OCP e4m3fn (bias 7, max 448, no inf) times a per-head fp32 scale */
+} bsp_dtype;
+
+/* Limits checked by every entry point. */
+#define BSP_MAX_HEADS 1024
+#define BSP_MAX_SEQ (1 << 21)
+
+/* Problem description, read on the host during the call only. */
+typedef struct bsp_desc {
+  int32_t hq;           /* query heads, 1..BSP_MAX_HEADS */
+  int32_t hkv;          /* key/value heads, divides hq */
+  int32_t seq;          /* tokens, 0..BSP_MAX_SEQ */
+  int32_t d;            /* head dimension: 64 or 128 */
+  int32_t block;        /* B, tokens per block: 64 or 128 (the page uses 128, Appendix A) */
+  float gamma;          /* threshold factor in [0, 1] (the page's alpha, section 3 / Appendix A) */
+  float sm_scale;       /* softmax scale c; <= 0 selects 1/sqrt(d); must be finite */
+  int32_t causal;       /* must be 1 (prefill attention is causal) */
+  int32_t sink_blocks;  /* leading key blocks always kept (>= 0); Appendix A keeps a sink */
+  int32_t local_blocks; /* key blocks ending at the diagonal always kept (>= 0); 1 = diagonal */
+  int32_t dtype;        /* bsp_dtype of Q, K and V */
+  const float *q_scale; /* fp8 only, device [hq]:  Q = code * q_scale[h] */
+  const float *k_scale; /* fp8 only, device [hkv]: K = code * k_scale[g] */
+  const float *v_scale; /* fp8 only, device [hkv]: V = code * v_scale[g] */
+} bsp_desc;
+
+/*
+ * bsp_score - stage 1, pattern discovery (FlashPrefill summary page, section 3
+ * "Instantaneous Pattern Discovery" and "Block Approximation"; Appendix B).
+ *
+ *   q_pool[h][I][:]  = mean of Q[h][t][:] over the tokens t of block I
+ *   k_pool[g][J][:]  = mean of K[g][t][:] over the tokens t of block J
+ *                      (fp8: means of the dequantised values)
+ *   S[h][I][J]       = c * q_pool[h][I] . k_pool[g(h)][J]          for J <= I
+ *   score[h][I][J]   = exp(S - max_J' S) / sum_J'<=I exp(S - max_J' S)  for J <= I
+ *   score[h][I][J]   = 0                                             for J > I
+ *
+ * q, k:    device, storage dtype, [hq][seq][d] and [hkv][seq][d]
+ * q_pool:  device float [hq][nb][d]     (written)
+ * k_pool:  device float [hkv][nb][d]    (written)
+ * score:   device float [hq][nb][nb]    (written, every entry)
+ * Needs desc->q_scale and desc->k_scale for fp8 (v_scale is not read).
+ */
+bsp_status bsp_score(const bsp_desc *desc, const void *q, const void *k, float *q_pool,
+                     float *k_pool, float *score, void *stream);
+
+/*
+ * bsp_mask - stage 2, max-based dynamic thresholding and block selection
+ * (section 3 "Max-based Dynamic Thresholding"; Appendix A structural
+ * retention; Appendix B "Dynamic Thresholding and Block Selection").
+ *
+ * Without user_mask, for J <= I:
+ *   keep[h][I][J] = score[h][I][J] >= gamma * max_J'<=I score[h][I][J']
+ *                   OR J < sink_blocks OR I - J < local_blocks
+ * With user_mask (device uint8 [hq][nb][nb], nonzero = keep), the threshold
+ * and the forced blocks are replaced by it: keep = user_mask != 0 AND J <= I.
+ * keep is 0 for J > I.  No sort and no cumulative sum is used.
+ *
+ * score:     device float [hq][nb][nb] as written by bsp_score; may be NULL
+ *            iff user_mask is given (then it is not read)
+ * user_mask: device uint8 [hq][nb][nb] or NULL
+ * mask:      device uint8 [hq][nb][nb] or NULL; written with keep (0/1)
+ * kv_idx:    device int32 [hq][nb][nb]; row (h, I) receives the kept J in
+ *            ascending order in its first kv_cnt[h][I] entries (the diagonal,
+ *            when kept, last); entries past the count are not written
+ * kv_cnt:    device int32 [hq][nb]
+ * Reads desc->gamma, sink_blocks, local_blocks, hq, seq, block (not dtype).
+ */
+bsp_status bsp_mask(const bsp_desc *desc, const float *score, const uint8_t *user_mask,
+                    uint8_t *mask, int32_t *kv_idx, int32_t *kv_cnt, void *stream);
+
+/*
+ * bsp_attn_fwd - stage 3, block-sparse attention (Appendix B "Block Sparse
+ * Attention": iterate only over the selected blocks, causal masking where
+ * required, online softmax, final normalisation).
+ *
+ * For every query token i of block I of head h, over the tokens j of the key
+ * blocks listed in kv_idx[h][I][0 .. kv_cnt[h][I]) with j <= i:
+ *   o[h][i][:] = sum_j softmax_j(c * q_i . k_j) * v_j[:]
+ *   lse[h][i]  = ln sum_j exp(c * q_i . k_j)      (natural log)
+ * An empty set gives o = 0 and lse = -inf.  Block indices must be distinct,
+ * in [0, I]; the order of a row does not change the result beyond rounding.
+ *
+ * q, k, v:  device, storage dtype; fp8 needs all three desc scales
+ * kv_idx, kv_cnt: device, as produced by bsp_mask; both NULL = dense causal
+ *           (every J <= I); one NULL and not the other is an error
+ * o:        device [hq][seq][d]; float for BSP_DTYPE_F32, bfloat16 otherwise
+ * lse:      device float [hq][seq], or NULL
+ * Arithmetic: f32 inputs use fp32 FMA; bf16 and fp8 use MFMA with fp32
+ * accumulation and an fp32 softmax.
+ */
+bsp_status bsp_attn_fwd(const bsp_desc *desc, const void *q, const void *k, const void *v,
+                        const int32_t *kv_idx, const int32_t *kv_cnt, void *o, float *lse,
+                        void *stream);
+
+/* Static description of a status code (host, never NULL). */
+const char *bsp_status_string(int32_t status);
+
+/* BSP_ABI_VERSION of the loaded library. */
+int32_t bsp_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* BSP_H */

@@ -1,0 +1,125 @@
+"""C-ABI checks that need no GPU: the library loads, exports every entry
+point include/bsp.h declares, and rejects bad arguments on the host before
+any launch (so these calls never reach the device)."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+import block_sparse_attention_bsp_amd as bsp
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "bsp.h")
+
+
+def _declared():
+    txt = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(bsp_\w+)\s*\(", txt, re.M)))
+
+
+@pytest.fixture(scope="module", autouse=True)
+def built():
+    if not os.path.exists(bsp.library_path):
+        from block_sparse_attention_bsp_amd import build
+        build.build()
+
+
+def test_header_declares_the_entry_points():
+    assert _declared() == ["bsp_abi_version", "bsp_attn_fwd", "bsp_mask", "bsp_score",
+                           "bsp_status_string"]
+
+
+def test_library_exports_every_declared_symbol():
+    out = subprocess.run(["nm", "-D", "--defined-only", bsp.library_path], capture_output=True,
+                         text=True, check=True).stdout
+    exported = set(re.findall(r"\s[TW]\s+(bsp_\w+)$", out, re.M))
+    for name in _declared():
+        assert name in exported, name
+        assert hasattr(bsp.lib(), name)
+
+
+def test_abi_version_matches_header():
+    want = int(re.search(r"#define BSP_ABI_VERSION (\d+)", open(HEADER).read()).group(1))
+    assert bsp.bsp_abi_version() == want
+
+
+def test_desc_struct_layout_matches_header():
+    # int32 x5, float x2, int32 x4, then three pointers (8-byte aligned)
+    assert ctypes.sizeof(bsp.BspDesc) == 11 * 4 + 4 + 3 * 8
+    assert bsp.BspDesc.q_scale.offset == 48
+
+
+def test_status_strings():
+    for code, name in [(0, "BSP_OK"), (1, "BSP_ERR_NULL_POINTER"), (2, "BSP_ERR_BAD_SHAPE"),
+                       (3, "BSP_ERR_BAD_DTYPE"), (4, "BSP_ERR_BAD_VALUE"),
+                       (5, "BSP_ERR_UNSUPPORTED"), (6, "BSP_ERR_HIP")]:
+        assert bsp.bsp_status_string(code).startswith(name)
+    assert "unknown" in bsp.bsp_status_string(99)
+
+
+FAKE = ctypes.c_void_p(0x1000)  # never dereferenced: every case below fails validation
+
+
+def _d(**kw):
+    base = dict(hq=4, hkv=2, seq=256, d=128, block=128, dtype=bsp.DTYPE_BF16, gamma=0.1)
+    base.update(kw)
+    return bsp.desc(**base)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(hq=0), 2), (dict(hkv=3), 2), (dict(hkv=8), 2), (dict(seq=-1), 2),
+    (dict(seq=(1 << 21) + 1), 2), (dict(d=96), 2), (dict(block=32), 2), (dict(causal=0), 5),
+    (dict(dtype=7), 3), (dict(sm_scale=float("inf")), 4), (dict(sm_scale=float("nan")), 4),
+])
+def test_score_rejects_bad_desc(kw, status):
+    assert bsp.bsp_score(_d(**kw), FAKE, FAKE, FAKE, FAKE, FAKE, None) == status
+
+
+def test_null_pointers_rejected():
+    assert bsp.lib().bsp_score(None, FAKE, FAKE, FAKE, FAKE, FAKE, None) == 1
+    assert bsp.bsp_score(_d(), None, FAKE, FAKE, FAKE, FAKE, None) == 1
+    assert bsp.bsp_score(_d(), FAKE, FAKE, FAKE, FAKE, None, None) == 1
+    assert bsp.bsp_mask(_d(), None, None, None, FAKE, FAKE, None) == 1
+    assert bsp.bsp_mask(_d(), FAKE, None, None, None, FAKE, None) == 1
+    assert bsp.bsp_attn_fwd(_d(), FAKE, FAKE, None, None, None, FAKE, None, None) == 1
+    # kv_idx and kv_cnt go together
+    assert bsp.bsp_attn_fwd(_d(), FAKE, FAKE, FAKE, FAKE, None, FAKE, None, None) == 1
+
+
+@pytest.mark.parametrize("gamma", [-0.1, 1.5, float("nan")])
+def test_mask_rejects_bad_gamma(gamma):
+    assert bsp.bsp_mask(_d(gamma=gamma), FAKE, None, None, FAKE, FAKE, None) == 4
+
+
+def test_mask_rejects_negative_windows():
+    assert bsp.bsp_mask(_d(sink_blocks=-1), FAKE, None, None, FAKE, FAKE, None) == 4
+    assert bsp.bsp_mask(_d(local_blocks=-2), FAKE, None, None, FAKE, FAKE, None) == 4
+
+
+def test_fp8_scale_rules():
+    fp8 = _d(dtype=bsp.DTYPE_FP8_E4M3)
+    assert bsp.bsp_score(fp8, FAKE, FAKE, FAKE, FAKE, FAKE, None) == 3
+    assert bsp.bsp_attn_fwd(fp8, FAKE, FAKE, FAKE, None, None, FAKE, None, None) == 3
+    withscale = _d()
+    withscale.q_scale = 0x2000
+    assert bsp.bsp_score(withscale, FAKE, FAKE, FAKE, FAKE, FAKE, None) == 3
+    half = _d(dtype=bsp.DTYPE_FP8_E4M3)
+    half.q_scale = 0x2000
+    half.k_scale = 0x2000
+    assert bsp.bsp_attn_fwd(half, FAKE, FAKE, FAKE, None, None, FAKE, None, None) == 3  # no v_scale
+
+
+def test_empty_sequence_is_a_no_op():
+    # seq == 0 is valid and launches nothing
+    assert bsp.bsp_score(_d(seq=0), FAKE, FAKE, FAKE, FAKE, FAKE, None) == 0
+    assert bsp.bsp_mask(_d(seq=0), FAKE, None, None, FAKE, FAKE, None) == 0
+    assert bsp.bsp_attn_fwd(_d(seq=0), FAKE, FAKE, FAKE, None, None, FAKE, None, None) == 0
+
+
+def test_python_layer_raises_bsp_error():
+    import torch
+    x = torch.zeros(2, 64, 64)
+    with pytest.raises(bsp.BspError):
+        bsp.score(x, x, 64)  # host tensors are rejected before the C call

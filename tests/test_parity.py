@@ -1,0 +1,198 @@
+"""GPU parity of the HIP path (through the C ABI) against the CPU oracle on
+small and medium seeded inputs: every stage, every dtype, several tiles,
+ragged tails, sparse masks and the method's degenerate cases."""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import block_sparse_attention_bsp_amd as bsp
+import gen
+import oracle
+from tests import gpu_helpers as H
+
+pytestmark = pytest.mark.gpu
+
+
+def announce(msg):
+    print(f"\n[case] {msg}", flush=True)
+
+
+def full_check(case, gamma=None, sink=1, local=1, rows=None):
+    """Stages 1-2 on every block; stage 3 given the oracle's mask."""
+    g = case.gamma if gamma is None else gamma
+    d, res = H.run_gpu_prefill(case, gamma=g, sink=sink, local=local)
+    orc = oracle.prefill(case, gamma=g, sink_blocks=sink, local_blocks=local, with_attn=False)
+    np.testing.assert_allclose(res["q_pool"].cpu().numpy(), orc["qbar"], rtol=1e-5, atol=2e-6)
+    np.testing.assert_allclose(res["k_pool"].cpu().numpy(), orc["kbar"], rtol=1e-5, atol=2e-6)
+    np.testing.assert_allclose(res["score"].cpu().numpy(), orc["P"], rtol=1e-4, atol=1e-6)
+    nband = H.check_mask(res["mask"].cpu().numpy(), res["kv_idx"].cpu().numpy(),
+                         res["kv_cnt"].cpu().numpy(), orc, g, sink, local)
+    # attention given the oracle's mask
+    idx, cnt = H.idx_from_mask(orc["mask"])
+    o, lse = bsp.attn_fwd(d["q"], d["k"], d["v"], case.block, torch.from_numpy(idx).cuda(),
+                          torch.from_numpy(cnt).cuda(), q_scale=d["q_scale"],
+                          k_scale=d["k_scale"], v_scale=d["v_scale"])
+    torch.cuda.synchronize()
+    oo, ol = oracle.attn(case.q, case.k, case.v, case.dtype, case.block, orc["mask"],
+                         q_scale=case.q_scale, k_scale=case.k_scale, v_scale=case.v_scale,
+                         rows=rows)
+    if rows is None:
+        go = o.float().cpu().numpy().reshape(-1, case.d)
+        gl = lse.cpu().numpy().reshape(-1)
+        oo = oo.reshape(-1, case.d)
+        ol = ol.reshape(-1)
+    else:
+        go, gl = H.gather_rows(o, lse, rows)
+    err = H.check_attn(go, gl, oo, ol, case.dtype)
+    dens = orc["mask"].sum() / (case.hq * case.nb * (case.nb + 1) / 2)
+    print(f"  density {dens:.3f} band blocks {nband} max-abs O err {err:.2e}", flush=True)
+    return res, orc
+
+
+def test_config0_tiny_fp32():
+    announce("config 0 tiny fp32")
+    full_check(gen.make_config(0))
+
+
+@pytest.mark.parametrize("seed", [0, 1, 2, 3])
+def test_s1_sparse_masks_fp32(seed):
+    announce(f"S1 seed {seed}")
+    full_check(gen.make_s1(seed))
+
+
+@pytest.mark.parametrize("dtype,d,block,seq", [
+    ("bf16", 128, 128, 1000), ("bf16", 64, 64, 777), ("bf16", 128, 64, 640),
+    ("bf16", 64, 128, 513), ("fp8", 128, 128, 1000), ("fp8", 64, 64, 700),
+    ("f32", 128, 128, 300), ("f32", 64, 128, 250), ("f32", 128, 64, 333),
+])
+def test_sparse_ragged_shapes(dtype, d, block, seq):
+    announce(f"sparse ragged {dtype} d={d} B={block} seq={seq}")
+    c = gen.make_case(8, 2, seq, d, block, dtype, 42 + seq, gamma=0.2, rope=True, n_vert=6,
+                      slash=True, block_offset=1.0)
+    full_check(c)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp8"])
+def test_config_shape_4k_sampled(dtype):
+    """Config 1 (or config 4's heads/dtype) at seq 4096: every head, sampled rows."""
+    announce(f"4K {dtype}")
+    c = gen.make_config(1) if dtype == "bf16" else gen.make_config(4, seq=4096)
+    rows = H.sample_rows(c.hq, c.seq, c.block, n_pos=16)
+    full_check(c, rows=rows)
+
+
+def test_gamma0_equals_dense_path_bitwise():
+    announce("gamma=0 vs dense")
+    c = gen.make_case(4, 2, 1024, 128, 128, "bf16", 5, rope=True, n_vert=4)
+    d, res = H.run_gpu_prefill(c, gamma=0.0)
+    nb = c.nb
+    assert torch.equal(res["kv_cnt"].cpu(), torch.arange(1, nb + 1, dtype=torch.int32).expand(4, nb))
+    o, lse = bsp.attn_fwd(d["q"], d["k"], d["v"], c.block)
+    torch.cuda.synchronize()
+    assert torch.equal(o, res["o"]) and torch.equal(lse, res["lse"])
+
+
+def test_user_mask_with_empty_rows():
+    announce("user mask, empty rows")
+    c = gen.make_case(4, 1, 640, 128, 128, "bf16", 8)
+    nb = c.nb
+    rng = np.random.default_rng(1)
+    um = (rng.random((4, nb, nb)) < 0.5).astype(np.uint8)
+    um[1, 2, :] = 0
+    um[3, :, :] = 0
+    d, res = H.run_gpu_prefill(c, user_mask=um)
+    m = res["mask"].cpu().numpy()
+    assert np.array_equal(m, um & np.tril(np.ones((nb, nb), np.uint8)))
+    oo, ol = oracle.attn(c.q, c.k, c.v, "bf16", c.block, m)
+    go = res["o"].float().cpu().numpy()
+    gl = res["lse"].cpu().numpy()
+    H.check_attn(go.reshape(-1, 128), gl.reshape(-1), oo.reshape(-1, 128), ol.reshape(-1), "bf16")
+    assert np.all(go[3] == 0) and np.all(np.isneginf(gl[3]))
+    assert np.all(go[1, 256:384] == 0)
+
+
+def test_rows_sum_to_one():
+    announce("V == 1")
+    c = gen.make_case(4, 2, 512, 128, 128, "bf16", 9, block_offset=1.0)
+    c.v[:] = gen.bf16_bits(np.ones(1, np.float32))[0]
+    d, res = H.run_gpu_prefill(c, gamma=0.3)
+    assert torch.all(res["o"].float() == 1.0)
+
+
+def test_index_order_does_not_matter():
+    announce("permuted kv_idx")
+    c = gen.make_case(4, 2, 1024, 128, 128, "bf16", 10)
+    d, res = H.run_gpu_prefill(c, gamma=0.0)
+    idx = res["kv_idx"].cpu().numpy().copy()
+    cnt = res["kv_cnt"].cpu().numpy()
+    rng = np.random.default_rng(0)
+    for h in range(4):
+        for I in range(c.nb):
+            idx[h, I, :cnt[h, I]] = rng.permutation(idx[h, I, :cnt[h, I]])
+    o, lse = bsp.attn_fwd(d["q"], d["k"], d["v"], c.block, torch.from_numpy(idx).cuda(),
+                          res["kv_cnt"])
+    torch.cuda.synchronize()
+    assert (o.float() - res["o"].float()).abs().max().item() <= 1e-2
+    assert (lse - res["lse"]).abs().max().item() <= 1e-4
+
+
+def test_duplicated_heads_and_mha_expansion():
+    announce("duplicated heads / MHA")
+    c = gen.make_case(4, 2, 512, 128, 128, "bf16", 11)
+    c.q[1] = c.q[0]
+    d, res = H.run_gpu_prefill(c, gamma=0.0)
+    assert torch.equal(res["o"][0], res["o"][1])
+    k4 = d["k"].repeat_interleave(2, dim=0).contiguous()
+    v4 = d["v"].repeat_interleave(2, dim=0).contiguous()
+    o4, _ = bsp.attn_fwd(d["q"], k4, v4, c.block)
+    torch.cuda.synchronize()
+    assert torch.equal(o4, res["o"])
+
+
+def test_deterministic():
+    announce("determinism")
+    c = gen.make_case(8, 2, 2048, 128, 128, "bf16", 12, rope=True, slash=True, block_offset=1.0)
+    _, a = H.run_gpu_prefill(c)
+    _, b = H.run_gpu_prefill(c)
+    for key in ("score", "mask", "kv_idx", "kv_cnt", "o", "lse"):
+        if key == "kv_idx":
+            cnt = a["kv_cnt"]
+            keep = torch.arange(c.nb, device=cnt.device)[None, None, :] < cnt[..., None]
+            assert torch.equal(a[key][keep], b[key][keep])
+        else:
+            assert torch.equal(a[key], b[key]), key
+
+
+def test_errors_leave_outputs_untouched():
+    announce("error path canaries")
+    q = torch.zeros(4, 256, 128, dtype=torch.bfloat16, device="cuda")
+    o = torch.full((4, 256, 128), 7.0, dtype=torch.bfloat16, device="cuda")
+    with pytest.raises(bsp.BspError) as e:
+        bsp.attn_fwd(q, q[:3].contiguous(), q[:3].contiguous(), 128, out=o)
+    assert e.value.status == 2
+    torch.cuda.synchronize()
+    assert torch.all(o == 7.0)
+
+
+def test_empty_sequence():
+    announce("seq = 0")
+    q = torch.zeros(4, 0, 128, dtype=torch.bfloat16, device="cuda")
+    o, lse = bsp.attn_fwd(q, q[:2], q[:2], 128)
+    qp, kp, sc = bsp.score(q, q[:2], 128)
+    assert o.shape == (4, 0, 128) and sc.shape == (4, 0, 0)
+
+
+def test_sm_scale_override():
+    announce("explicit sm_scale")
+    c = gen.make_case(2, 1, 256, 64, 64, "bf16", 13)
+    d = H.dev(c)
+    bm = np.tril(np.ones((2, 4, 4), np.uint8))
+    idx, cnt = H.idx_from_mask(bm)
+    o, lse = bsp.attn_fwd(d["q"], d["k"], d["v"], 64, torch.from_numpy(idx).cuda(),
+                          torch.from_numpy(cnt).cuda(), sm_scale=0.3)
+    torch.cuda.synchronize()
+    oo, ol = oracle.attn(c.q, c.k, c.v, "bf16", 64, bm, sm_scale=0.3)
+    H.check_attn(o.float().cpu().numpy().reshape(-1, 64), lse.cpu().numpy().reshape(-1),
+                 oo.reshape(-1, 64), ol.reshape(-1), "bf16")

@@ -1,0 +1,41 @@
+"""GPU parity at the measured layer sizes, in the launch configuration the
+benchmark times (score -> mask -> attention on the GPU's own mask): every
+block of the pooled values, scores and masks, and sampled output rows that
+the oracle computes one by one."""
+import time
+
+import numpy as np
+import pytest
+import torch
+
+import gen
+import oracle
+from tests import gpu_helpers as H
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.mark.parametrize("cfg", [1, 2, 3, 4])
+def test_config_full_size(cfg):
+    t0 = time.time()
+    print(f"\n[case] config {cfg} ({gen.CONFIGS[cfg]['name']}) full size", flush=True)
+    c = gen.make_config(cfg)
+    print(f"  generated in {time.time() - t0:.1f}s", flush=True)
+    d, res = H.run_gpu_prefill(c)
+    print(f"  gpu prefill done {time.time() - t0:.1f}s", flush=True)
+    orc = oracle.prefill(c, with_attn=False)
+    print(f"  oracle stages 1-2 done {time.time() - t0:.1f}s", flush=True)
+    np.testing.assert_allclose(res["q_pool"].cpu().numpy(), orc["qbar"], rtol=1e-5, atol=2e-6)
+    np.testing.assert_allclose(res["k_pool"].cpu().numpy(), orc["kbar"], rtol=1e-5, atol=2e-6)
+    np.testing.assert_allclose(res["score"].cpu().numpy(), orc["P"], rtol=1e-4, atol=1e-6)
+    gm = res["mask"].cpu().numpy()
+    nband = H.check_mask(gm, res["kv_idx"].cpu().numpy(), res["kv_cnt"].cpu().numpy(), orc,
+                         c.gamma)
+    rows = H.sample_rows(c.hq, c.seq, c.block, n_pos=12, seed=cfg)
+    oo, ol = oracle.attn(c.q, c.k, c.v, c.dtype, c.block, gm, q_scale=c.q_scale,
+                         k_scale=c.k_scale, v_scale=c.v_scale, rows=rows)
+    go, gl = H.gather_rows(res["o"], res["lse"], rows)
+    err = H.check_attn(go, gl, oo, ol, c.dtype)
+    dens = gm.sum() / (c.hq * c.nb * (c.nb + 1) / 2)
+    print(f"  density {dens:.4f} band {nband} rows {rows.size} max-abs O err {err:.2e} "
+          f"total {time.time() - t0:.1f}s", flush=True)
