@@ -1,0 +1,257 @@
+"""Benchmark: dynamic block-sparse causal prefill attention, one layer.
+
+One step = the whole hot path on one batch of synthetic input already
+resident in HBM: bsp_score (pool Q/K + block scores), bsp_mask (dynamic
+threshold + index compaction), bsp_attn_fwd (block-sparse attention).
+
+Default workload: a Llama-3-8B-shaped layer at 128K tokens - 32 q / 8 kv
+heads, d = 128, block 128, gamma 0.05, causal, bf16, batch 1 - with the
+seeded RoPE + vertical + slash generator (gen.make_config(3)).
+
+Prints one JSON line.  value = effective TFLOP/s of the step, i.e. the
+dense-causal FLOPs 4*d*hq*L(L+1)/2 divided by the step time; ms_per_step is
+the ms per layer.  The roofline object describes the attention kernel, the
+dominant one: achieved = kept-block FLOPs per launch / mean launch time
+(HIP events on the stream the kernel runs on) against the dense bf16 MFMA
+peak.  cpu_baseline times the CPU oracle on a bounded row sample of the same
+layer on the host.
+
+Only one GPU is used: --gpus above 1 exits with a message.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import re
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+PEAK_FP8_TFLOPS = 5000.0    # MI355X dense fp8 MFMA
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+ATTN_SRC = os.path.join(ROOT, "block_sparse_attention_bsp_amd", "csrc", "attn_mfma.hip")
+PMC_NOTE = os.path.join(ROOT, "profiles", "attn_mfma_bf16_llama128k_pmc.md")
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=5)
+    p.add_argument("--warmup", type=int, default=2)
+    p.add_argument("--config", type=int, default=3, help="layer config index (gen.CONFIGS)")
+    p.add_argument("--seq", type=int, default=None, help="override sequence length")
+    p.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    p.add_argument("--cpu-rows", type=int, default=8192, help="query rows in the CPU sample")
+    p.add_argument("--user-density", type=float, default=None,
+                   help="replace the scorer by a random caller mask of this density")
+    p.add_argument("--copy-calibration", action="store_true",
+                   help="also run one 1 GiB device copy (HBM counter calibration)")
+    return p.parse_args()
+
+
+def dense_flops(hq, seq, d):
+    return 4.0 * d * hq * seq * (seq + 1) / 2.0
+
+
+def kept_flops(cnt: np.ndarray, d: int, block: int, seq: int) -> float:
+    """4*d*sum over kept (h, I, J) of the causal pairs in the tile (B^2 off
+    the diagonal, B(B+1)/2 on it; ragged tails are not in the configs)."""
+    nb = cnt.shape[1]
+    tot = cnt.astype(np.float64).sum()
+    diag = cnt.shape[0] * nb  # the diagonal is always kept (local window of 1)
+    return 4.0 * d * ((tot - diag) * block * block + diag * block * (block + 1) / 2.0)
+
+
+def scoring_bytes(hq, hkv, seq, d, block, es, kept_entries):
+    nb = -(-seq // block)
+    rd = (hq + hkv) * seq * d * es                   # read Q, K
+    wr_pool = (hq + hkv) * nb * d * 4                 # write pooled rows
+    p = hq * nb * nb * 4                              # write P, read P
+    mask = hq * nb * nb                               # write mask
+    idx = kept_entries * 4 + hq * nb * 4              # write idx (kept) and counts
+    return rd + wr_pool + 2 * p + mask + idx
+
+
+def traffic_from_note():
+    """HBM bytes per attention launch from the committed counter summary, if
+    it was taken on the current kernel source (else None)."""
+    if not os.path.exists(PMC_NOTE):
+        return None
+    txt = open(PMC_NOTE).read()
+    m_sha = re.search(r"source_sha256:\s*([0-9a-f]{64})", txt)
+    m_b = re.search(r"traffic_bytes_per_launch:\s*([0-9.eE+]+)", txt)
+    if not m_sha or not m_b:
+        return None
+    cur = hashlib.sha256(open(ATTN_SRC, "rb").read()).hexdigest()
+    return float(m_b.group(1)) if cur == m_sha.group(1) else None
+
+
+def cpu_baseline(case, gpu_mask, nrows):
+    """Oracle (as it stands) on the host: stages 1-2 on the whole layer, stage
+    3 on a uniform sample of query rows; extrapolated to the layer by FLOPs."""
+    import oracle
+    t0 = time.perf_counter()
+    orc = oracle.prefill(case, with_attn=False)
+    t12 = time.perf_counter() - t0
+    per_head = max(1, nrows // case.hq)
+    pos = np.unique(np.linspace(0, case.seq - 1, per_head).astype(np.int64))
+    rows = (np.arange(case.hq)[:, None] * case.seq + pos[None, :]).reshape(-1)
+    t0 = time.perf_counter()
+    oracle.attn(case.q, case.k, case.v, case.dtype, case.block, orc["mask"],
+                q_scale=case.q_scale, k_scale=case.k_scale, v_scale=case.v_scale, rows=rows)
+    t3 = time.perf_counter() - t0
+    # dense-causal work of the sampled rows: query i sees i+1 keys
+    samp = 4.0 * case.d * float((pos + 1).sum()) * case.hq
+    full = dense_flops(case.hq, case.seq, case.d)
+    t_layer = t12 + t3 * full / samp
+    return {
+        "value": round(full / t_layer / 1e12, 6), "unit": "TFLOP/s", "cores": oracle.threads(),
+        "kind": "oracle",
+        "sample": (f"pool+score+mask on the whole layer ({t12:.2f}s) + attention for "
+                   f"{rows.size} query rows ({per_head} uniformly spaced per head, {t3:.2f}s), "
+                   f"extrapolated by dense-causal FLOPs to one layer = {t_layer:.1f}s"),
+    }
+
+
+def main():
+    a = parse()
+    if a.gpus != 1:
+        print(f"bench.py runs on exactly one GPU; --gpus {a.gpus} is not supported "
+              "(this library runs its hot path on one GPU)",
+              file=sys.stderr)
+        sys.exit(2)
+    import torch
+    import block_sparse_attention_bsp_amd as bsp
+    import gen
+
+    if not os.path.exists(bsp.library_path):
+        from block_sparse_attention_bsp_amd import build
+        build.build()
+    assert torch.cuda.is_available(), "needs a GPU"
+    torch.cuda.set_device(0)
+
+    c = gen.make_config(a.config, seq=a.seq)
+    hq, hkv, seq, d, B = c.hq, c.hkv, c.seq, c.d, c.block
+    nb = c.nb
+
+    def t(x):
+        if c.dtype == "bf16":
+            return torch.from_numpy(x.view(np.int16)).cuda().view(torch.bfloat16)
+        return torch.from_numpy(x).cuda()
+    q, k, v = t(c.q), t(c.k), t(c.v)
+    qs = ks = vs = None
+    if c.dtype == "fp8":
+        qs, ks, vs = (torch.from_numpy(x).cuda() for x in (c.q_scale, c.k_scale, c.v_scale))
+    um = None
+    if a.user_density is not None:
+        um = torch.from_numpy(gen.random_block_mask(hq, nb, a.user_density, 0)).cuda()
+
+    # preallocated outputs: the timed region only launches kernels
+    f32, dev = torch.float32, "cuda"
+    qp = torch.empty((hq, nb, d), dtype=f32, device=dev)
+    kp = torch.empty((hkv, nb, d), dtype=f32, device=dev)
+    sc = torch.empty((hq, nb, nb), dtype=f32, device=dev)
+    mk = torch.empty((hq, nb, nb), dtype=torch.uint8, device=dev)
+    idx = torch.empty((hq, nb, nb), dtype=torch.int32, device=dev)
+    cnt = torch.empty((hq, nb), dtype=torch.int32, device=dev)
+    o = torch.empty((hq, seq, d), dtype=f32 if c.dtype == "f32" else torch.bfloat16, device=dev)
+    lse = torch.empty((hq, seq), dtype=f32, device=dev)
+    dsc = bsp.desc(hq, hkv, seq, d, B, {"f32": 0, "bf16": 1, "fp8": 2}[c.dtype], gamma=c.gamma,
+                   q_scale=qs, k_scale=ks, v_scale=vs)
+    P = bsp._ptr
+    stream = torch.cuda.current_stream()
+    sp = bsp._stream()
+
+    def step(ev=None):
+        if ev:
+            ev[0].record(stream)
+        if um is None:
+            bsp._check(bsp.bsp_score(dsc, P(q), P(k), P(qp), P(kp), P(sc), sp))
+        if ev:
+            ev[1].record(stream)
+        bsp._check(bsp.bsp_mask(dsc, None if um is not None else P(sc), P(um), P(mk), P(idx),
+                                P(cnt), sp))
+        if ev:
+            ev[2].record(stream)
+        bsp._check(bsp.bsp_attn_fwd(dsc, P(q), P(k), P(v), P(idx), P(cnt), P(o), P(lse), sp))
+        if ev:
+            ev[3].record(stream)
+
+    for _ in range(a.warmup):
+        step()
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(a.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(a.steps):
+        step(evs[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_step = wall * 1e3 / a.steps
+    st_score = float(np.mean([e[0].elapsed_time(e[1]) for e in evs]))
+    st_mask = float(np.mean([e[1].elapsed_time(e[2]) for e in evs]))
+    st_attn = float(np.mean([e[2].elapsed_time(e[3]) for e in evs]))
+
+    cnt_h = cnt.cpu().numpy()
+    kept_entries = int(cnt_h.sum())
+    density = kept_entries / (hq * nb * (nb + 1) / 2)
+    F_dense = dense_flops(hq, seq, d)
+    F_kept = kept_flops(cnt_h, d, B, seq)
+    peak = PEAK_FP8_TFLOPS if c.dtype == "fp8" else PEAK_BF16_TFLOPS
+    achieved = F_kept / (st_attn * 1e-3) / 1e12
+    es = {"f32": 4, "bf16": 2, "fp8": 1}[c.dtype]
+    sbytes = scoring_bytes(hq, hkv, seq, d, B, es, kept_entries)
+    score_gbs = sbytes / ((st_score + st_mask) * 1e-3) / 1e9
+
+    if a.copy_calibration:
+        src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+
+    cpu = None
+    if not a.no_cpu:
+        cpu = cpu_baseline(c, mk.cpu().numpy(), a.cpu_rows)
+
+    traffic = traffic_from_note() if (a.config == 3 and a.seq is None and um is None) else None
+    wl = (f"{c.name}: {hq} q / {hkv} kv heads, seq {seq}, d {d}, block {B}, gamma {c.gamma}, "
+          f"causal, {c.dtype}, batch 1, one layer")
+    if um is not None:
+        wl += f", caller mask density {a.user_density}"
+    out = {
+        "metric": "sparse prefill-attn ms/layer + effective TFLOP/s at 128K bf16; % MFMA peak",
+        "value": round(F_dense / (ms_step * 1e-3) / 1e12, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1, "steps": a.steps, "warmup": a.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": c.dtype, "data": "synthetic (seeded RoPE + planted vertical/slash generator)",
+        "config": {"workload": wl, "hq": hq, "hkv": hkv, "seq_len": seq, "head_dim": d,
+                   "block": B, "gamma": c.gamma, "batch": 1, "parallelism": "none (1 GPU)"},
+        "ms_per_layer": round(ms_step, 4),
+        "stage_ms": {"score": round(st_score, 4), "mask": round(st_mask, 4),
+                     "attn": round(st_attn, 4)},
+        "density": round(density, 6),
+        "kept_tflops": round(achieved, 3),
+        "mfma_peak_frac": round(achieved / peak, 4),
+        "scoring": {"bytes": sbytes, "GB/s": round(score_gbs, 1),
+                    "hbm_frac": round(score_gbs / PEAK_HBM_GBS, 4)},
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 3), "peak": peak,
+                     "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
+                     "traffic": traffic, "kernel": "attn_mfma_kernel",
+                     "flops_per_launch": F_kept},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -7,23 +7,31 @@
 //
 // gfx950 design
 //   * One workgroup per (q head, query block I): B/32 wavefronts, each owning
-//     32 queries, whose Q fragments stay in registers for the whole row.
+//     32 queries whose Q fragments stay in registers for the whole row.  Two
+//     workgroups share a CU (2 waves per SIMD) so one wave's MFMAs overlap the
+//     other's softmax.
+//   * Workgroups are numbered heaviest row first and, when the kv heads divide
+//     the 8 XCDs evenly, every XCD serves whole GQA groups: the 64 workgroups
+//     resident on an XCD walk the same K/V blocks in the same order, so K/V
+//     come from that XCD's L2.
 //   * Scores are computed transposed, S^T = K Q^T (v_mfma_f32_32x32x16_bf16,
-//     or v_mfma_scale_f32_32x32x64_f8f6f4 with unit scales for e4m3): in the
-//     32x32 result every lane holds one query and 16 keys, so the softmax row
-//     max and row sum are in-lane plus one exchange with the lane 32 away.
-//   * The output is accumulated transposed, O^T += V^T P^T (bf16 MFMA), so
-//     each lane's accumulators belong to its own query and the online-softmax
-//     rescale is a per-lane scalar.  P^T is the B operand straight from the
-//     score registers; the key order within a 16-key step is permuted the same
-//     way on both operands.
-//   * K and V sub-tiles of 64 keys are staged through LDS.  K rows carry an
-//     XOR swizzle of their read units (conflict-free 16/32-byte reads).  V is
-//     stored row-major as bf16 (fp8 codes are widened exactly) and read with
-//     ds_read_b64_tr_b16, whose 4x16 transpose hands each lane one d column
-//     of four consecutive keys - the V^T operand without a transposed copy.
-//   * Softmax in fp32 with exp2 (log2 e and, for fp8, the q/k scales folded
-//     into one factor); the v scale is applied at the final normalisation.
+//     or v_mfma_scale_f32_32x32x64_f8f6f4 with unit scales for e4m3): each lane
+//     holds one query and 16 keys of a 32x32 tile, so the softmax reductions
+//     are in-lane plus one exchange with the lane 32 away.
+//   * The output is accumulated transposed, O^T += V^T P^T (bf16 MFMA): every
+//     accumulator of a lane belongs to its own query.  P^T is the B operand
+//     straight from the score registers; the key order inside a 16-key step is
+//     permuted identically on both operands.
+//   * K/V sub-tiles of 64 keys are double-buffered in LDS and filled by
+//     global_load_lds_dwordx4 (no VGPR staging) one sub-tile ahead, so the
+//     load of sub-tile i+1 overlaps the MFMAs of sub-tile i; one barrier per
+//     sub-tile.  K rows carry an XOR swizzle of their read units; V is stored
+//     row-major bf16 (fp8 codes are widened exactly on the way in) and read
+//     with ds_read_b64_tr_b16, whose 4x16 transpose yields the V^T operand.
+//   * Softmax in fp32, exp2 domain with log2(e) and (fp8) the q/k scales in
+//     one factor; the max is taken on raw scores (max3), the exponent is one
+//     FMA, and the output is rescaled only when the running max grows by more
+//     than 2^8.
 #include <type_traits>
 
 #include "device.h"
@@ -32,6 +40,11 @@
 namespace bsp {
 
 typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+// Rescale the accumulators only when the running max grows by more than this
+// (log2 units): probabilities then stay below 2^8, well inside bf16/fp32.
+constexpr float kRescaleSlack = 8.0f;
 
 template <int DT, int D, int BLK>
 struct AttnCfg {
@@ -39,17 +52,20 @@ struct AttnCfg {
   static constexpr int RB = D * ES;              // bytes per K row
   static constexpr int KSTEP = DT == kFP8 ? 64 : 16;
   static constexpr int LB = KSTEP / 2 * ES;      // bytes per lane per S^T step (16 or 32)
+  static constexpr int CPU = LB / 16;            // 16-byte chunks per read unit
   static constexpr int DK = D / KSTEP;           // S^T k-steps
   static constexpr int UNITS = RB / LB;          // read units per K row
   static constexpr int KRPW = RB >= 256 ? 1 : 256 / RB;  // K rows per 256-byte window
-  static constexpr int VCH = D / 8;              // 16-byte chunks per bf16 V row
-  static constexpr int VRPW = D >= 128 ? 1 : 128 / D;
   static constexpr int NW = BLK / 32;
   static constexpr int NT = NW * 64;
   static constexpr int KT = 64;                  // keys per LDS sub-tile
   static constexpr int NSUB = BLK / KT;
   static constexpr int KTS = KT / 32;
   static constexpr int DTL = D / 32;
+  static constexpr int KBYTES = KT * RB;         // K sub-tile bytes
+  static constexpr int VBYTES = KT * D * 2;      // V sub-tile bytes (bf16)
+  static constexpr int KCH = KBYTES / 16;        // 16-byte chunks per K sub-tile
+  static constexpr int VCHK = KT * RB / 16;      // 16-byte global chunks per V sub-tile
 };
 
 template <int DT, int D, int BLK>
@@ -58,10 +74,15 @@ __device__ __forceinline__ int k_unit(int r, int u) {
   return u ^ ((r / C::KRPW) % C::UNITS);
 }
 
+// V rows are split into 64-byte groups; the group index is XORed with the
+// row so the four rows a ds_read_b64_tr_b16 lane group touches hit distinct
+// banks, while a 64-byte group stays contiguous.  Invariant under +4 rows
+// (d = 128) / +8 rows (d = 64), so per-lane offsets are loop constants.
 template <int D>
 __device__ __forceinline__ int v_chunk(int r, int c) {
-  constexpr int VCH = D / 8, VRPW = D >= 128 ? 1 : 128 / D;
-  return c ^ (((r / VRPW) % (VCH / 2)) * 2);
+  constexpr int VRPW = D >= 128 ? 1 : 128 / D;  // rows per 256-byte window
+  constexpr int NG = D / 32;                     // 64-byte groups per row
+  return c ^ (((r / VRPW) % NG) << 2);
 }
 
 __device__ __forceinline__ uint32_t e4m3_pair_to_bf16(uint32_t two) {
@@ -70,170 +91,332 @@ __device__ __forceinline__ uint32_t e4m3_pair_to_bf16(uint32_t two) {
          (__float_as_uint(e4m3_to_f32((two >> 8) & 0xFFu)) & 0xFFFF0000u);
 }
 
+__device__ __forceinline__ void lds_dma16(const void *gsrc, void *ldst) {
+  __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void *)gsrc,
+                                   (__attribute__((address_space(3))) void *)ldst, 16, 0, 0);
+}
+
 template <int DT, int D, int BLK>
-__global__ __launch_bounds__(BLK * 2) void attn_mfma_kernel(
-    const uint8_t *__restrict__ q, const uint8_t *__restrict__ k, const uint8_t *__restrict__ v,
-    const int32_t *__restrict__ kv_idx, const int32_t *__restrict__ kv_cnt,
-    uint16_t *__restrict__ o, float *__restrict__ lse, const float *__restrict__ q_scale,
-    const float *__restrict__ k_scale, const float *__restrict__ v_scale, int hq, int hkv,
-    int seq, int nb, float sm_scale_log2) {
+struct Attn {
   using C = AttnCfg<DT, D, BLK>;
-  constexpr int ES = C::ES, RB = C::RB, LB = C::LB, DK = C::DK, KT = C::KT, NT = C::NT;
-  constexpr int KTS = C::KTS, DTL = C::DTL;
-  __shared__ __attribute__((aligned(16))) uint8_t Ks[KT * RB];
-  __shared__ __attribute__((aligned(16))) uint16_t Vs[KT * D];
-
-  const int tid = threadIdx.x;
-  const int lane = tid & 63, w = tid >> 6, half = lane >> 5, l32 = lane & 31;
-  const int bid = blockIdx.x;
-  const int I = nb - 1 - bid / hq;
-  const int h = bid % hq;
-  const int g = h / (hq / hkv);
-  const int qi = I * BLK + w * 32 + l32;
-  const size_t row = (size_t)h * nb + I;
-  float scale2 = sm_scale_log2;
-  if constexpr (DT == kFP8) scale2 *= q_scale[h] * k_scale[g];
-
-  // Q fragments: B operand of S^T = K Q^T, query qi, LB bytes per step.
+  static constexpr int RB = C::RB, LB = C::LB, DK = C::DK, KT = C::KT;
+  static constexpr int KTS = C::KTS, DTL = C::DTL, NSUB = C::NSUB, NW = C::NW, NT = C::NT;
+  static constexpr int KPW = C::KCH / NW;               // K DMA chunks per wave
+  static constexpr int VPW = (C::VBYTES / 16) / NW;     // V DMA chunks per wave (bf16)
+  static constexpr int VPER = C::VCHK / NT > 0 ? C::VCHK / NT : 1;  // fp8 V chunks per thread
   typedef typename std::conditional<DT == kFP8, i32x8, bf16x8>::type frag_t;
+
+  const uint8_t *k, *v;
+  int seq, I, w, lane, half, l32, qi;
+  size_t kvrow0;  // g * seq
+  float scale2;
   frag_t qf[DK];
+  f32x16 oacc[DTL];
+  float m_used, l;
+  // per-lane byte offsets (loop constants)
+  int kdma[KPW / 64], vdma[DT == kBF16 ? VPW / 64 : 1], krow[KPW / 64], vrow[DT == kBF16 ? VPW / 64 : 1];
+  int koff[DK], voff[DTL];
+  uint4 vreg[VPER];
+
+  __device__ __forceinline__ void setup() {
 #pragma unroll
-  for (int kk = 0; kk < DK; ++kk) {
-    const uint8_t *src = q + ((size_t)h * seq + qi) * RB + kk * 2 * LB + half * LB;
-    uint4 a = make_uint4(0, 0, 0, 0), b = a;
-    if (qi < seq) {
-      a = *(const uint4 *)src;
-      if constexpr (LB == 32) b = *(const uint4 *)(src + 16);
+    for (int it = 0; it < KPW / 64; ++it) {
+      const int p = w * KPW + it * 64 + lane;
+      const int r = p / (RB / 16), pc = p % (RB / 16);
+      const int c = k_unit<DT, D, BLK>(r, pc / C::CPU) * C::CPU + pc % C::CPU;
+      kdma[it] = r * RB + c * 16;
+      krow[it] = r;
     }
-    if constexpr (LB == 32) {
-      const uint4 ab[2] = {a, b};
-      __builtin_memcpy(&qf[kk], ab, 32);
-    } else {
-      __builtin_memcpy(&qf[kk], &a, 16);
+    if constexpr (DT == kBF16) {
+#pragma unroll
+      for (int it = 0; it < VPW / 64; ++it) {
+        const int p = w * VPW + it * 64 + lane;
+        const int r = p / (D / 8), pc = p % (D / 8);
+        vdma[it] = r * (D * 2) + v_chunk<D>(r, pc) * 16;  // the swizzle is an involution
+        vrow[it] = r;
+      }
+    }
+#pragma unroll
+    for (int kk = 0; kk < DK; ++kk) koff[kk] = l32 * RB + k_unit<DT, D, BLK>(l32, kk * 2 + half) * LB;
+    const int vg = lane >> 4, vi = lane & 15, vrr = vi >> 2, vss = vi & 3;
+    const int r0 = (vg >> 1) * 4 + vrr;
+#pragma unroll
+    for (int db = 0; db < DTL; ++db) {
+      const int dcol = db * 32 + (vg & 1) * 16 + vss * 4;
+      voff[db] = r0 * (D * 2) + v_chunk<D>(r0, dcol >> 3) * 16 + (dcol & 7) * 2;
     }
   }
 
-  f32x16 oacc[DTL];
+  // Sub-tile (J, sub) -> LDS buffers, issued one sub-tile ahead.  K (and bf16
+  // V) go straight to LDS; fp8 V comes back in registers for widening.
+  __device__ __forceinline__ void issue(int J, int sub, uint8_t *Kb, uint16_t *Vb) {
+    const int j0 = J * BLK + sub * KT;
+    const uint8_t *kb = k + (kvrow0 + j0) * RB;
+    const uint8_t *vb = v + (kvrow0 + j0) * (DT == kBF16 ? D * 2 : RB);
+    if (j0 + KT <= seq) {
 #pragma unroll
-  for (int db = 0; db < DTL; ++db) oacc[db] = f32x16{};
-  float m = -INFINITY, l = 0.f;
-
-  const int n = kv_idx ? min(kv_cnt[row], nb) : I + 1;
-  for (int t = 0; t < n; ++t) {
-    const int J = kv_idx ? kv_idx[row * nb + t] : t;
-    if (J < 0 || J > I) continue;
-    const bool diag = J == I;
-    for (int sub = 0; sub < C::NSUB; ++sub) {
-      const int j0 = J * BLK + sub * KT;
-      __syncthreads();
-      // ---- stage K (swizzled read units) and V (bf16, swizzled chunks)
-      for (int e = tid; e < KT * RB / 16; e += NT) {
-        const int r = e / (RB / 16), c = e % (RB / 16);
-        uint4 kv4 = make_uint4(0, 0, 0, 0), vv4 = kv4;
-        if (j0 + r < seq) {
-          const size_t goff = ((size_t)g * seq + j0 + r) * RB + c * 16;
-          kv4 = *(const uint4 *)(k + goff);
-          vv4 = *(const uint4 *)(v + goff);
-        }
-        constexpr int CPU = LB / 16;  // 16-byte chunks per read unit
-        const int pu = k_unit<DT, D, BLK>(r, c / CPU);
-        *(uint4 *)&Ks[r * RB + pu * LB + (c % CPU) * 16] = kv4;
-        if constexpr (DT == kFP8) {
-          const uint4 lo = make_uint4(e4m3_pair_to_bf16(vv4.x), e4m3_pair_to_bf16(vv4.x >> 16),
-                                      e4m3_pair_to_bf16(vv4.y), e4m3_pair_to_bf16(vv4.y >> 16));
-          const uint4 hi = make_uint4(e4m3_pair_to_bf16(vv4.z), e4m3_pair_to_bf16(vv4.z >> 16),
-                                      e4m3_pair_to_bf16(vv4.w), e4m3_pair_to_bf16(vv4.w >> 16));
-          *(uint4 *)&Vs[r * D + v_chunk<D>(r, 2 * c) * 8] = lo;
-          *(uint4 *)&Vs[r * D + v_chunk<D>(r, 2 * c + 1) * 8] = hi;
-        } else {
-          *(uint4 *)&Vs[r * D + v_chunk<D>(r, c) * 8] = vv4;
-        }
+      for (int it = 0; it < KPW / 64; ++it) lds_dma16(kb + kdma[it], Kb + (w * KPW + it * 64) * 16);
+      if constexpr (DT == kBF16) {
+#pragma unroll
+        for (int it = 0; it < VPW / 64; ++it)
+          lds_dma16(vb + vdma[it], (uint8_t *)Vb + (w * VPW + it * 64) * 16);
       }
-      __syncthreads();
+    } else {
+      // ragged last block: rows past the end re-read the last row (finite data
+      // whose keys are masked as causal-future for every valid query)
+#pragma unroll
+      for (int it = 0; it < KPW / 64; ++it)
+        lds_dma16(kb + kdma[it] - max(0, j0 + krow[it] - (seq - 1)) * RB,
+                  Kb + (w * KPW + it * 64) * 16);
+      if constexpr (DT == kBF16) {
+#pragma unroll
+        for (int it = 0; it < VPW / 64; ++it)
+          lds_dma16(vb + vdma[it] - max(0, j0 + vrow[it] - (seq - 1)) * (D * 2),
+                    (uint8_t *)Vb + (w * VPW + it * 64) * 16);
+      }
+    }
+    if constexpr (DT == kFP8) {
+#pragma unroll
+      for (int it = 0; it < VPER; ++it) {
+        const int e = threadIdx.x + it * NT;
+        const int r = e / (RB / 16), c = e % (RB / 16);
+        const int jr = min(j0 + r, seq - 1);
+        vreg[it] = *(const uint4 *)(v + (kvrow0 + jr) * RB + c * 16);
+      }
+    }
+  }
 
-      // ---- S^T tiles: rows = keys of the sub-tile, columns = the wave's queries
-      f32x16 s[KTS];
+  // fp8 only: widen the prefetched V codes to bf16 into the LDS buffer.
+  __device__ __forceinline__ void store_v(uint16_t *Vb) {
+    if constexpr (DT == kFP8) {
+#pragma unroll
+      for (int it = 0; it < VPER; ++it) {
+        const int e = threadIdx.x + it * NT;
+        const int r = e / (RB / 16), c = e % (RB / 16);
+        const uint4 vv4 = vreg[it];
+        const uint4 lo = make_uint4(e4m3_pair_to_bf16(vv4.x), e4m3_pair_to_bf16(vv4.x >> 16),
+                                    e4m3_pair_to_bf16(vv4.y), e4m3_pair_to_bf16(vv4.y >> 16));
+        const uint4 hi = make_uint4(e4m3_pair_to_bf16(vv4.z), e4m3_pair_to_bf16(vv4.z >> 16),
+                                    e4m3_pair_to_bf16(vv4.w), e4m3_pair_to_bf16(vv4.w >> 16));
+        *(uint4 *)&Vb[r * D + v_chunk<D>(r, 2 * c) * 8] = lo;
+        *(uint4 *)&Vb[r * D + v_chunk<D>(r, 2 * c + 1) * 8] = hi;
+      }
+    }
+  }
+
+  __device__ __forceinline__ void mask_diag(f32x16 (&s)[KTS], int j0) {
+    // Element r of tile kt is key j0 + kt*32 + (r/4)*8 + half*4 + r%4.
+#pragma unroll
+    for (int kt = 0; kt < KTS; ++kt)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int key = j0 + kt * 32 + (r / 4) * 8 + half * 4 + (r % 4);
+        if (key > qi) s[kt][r] = -INFINITY;
+      }
+  }
+
+  __device__ __forceinline__ void load_k(frag_t (&a)[KTS], const uint8_t *__restrict__ Kb, int kk) {
+#pragma unroll
+    for (int kt = 0; kt < KTS; ++kt)
+      __builtin_memcpy(&a[kt], Kb + koff[kk] + kt * 32 * RB, sizeof(frag_t));
+  }
+
+  __device__ __forceinline__ void load_v(bf16x8 (&a)[DTL], const uint16_t *__restrict__ Vb, int j) {
+    // step j = (kt, st) covers keys j*16 + [0, 16)
+#pragma unroll
+    for (int db = 0; db < DTL; ++db) {
+      const uint8_t *p0 = (const uint8_t *)Vb + voff[db] + j * 16 * (D * 2);
+      const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4 *)p0);
+      const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4 *)(p0 + 8 * D * 2));
+      a[db] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+    }
+  }
+
+  // One 64-key sub-tile from LDS.  LDS fragments are double-buffered in
+  // registers one MFMA group ahead; scheduling barriers keep that order.
+  __device__ __forceinline__ void compute(const uint8_t *__restrict__ Kb,
+                                          const uint16_t *__restrict__ Vb, int j0, bool diag) {
+    constexpr int NJ = KTS * 2;  // 16-key PV steps per sub-tile
+    // ---- S^T = K Q^T; the KTS accumulators alternate between MFMAs
+    f32x16 s[KTS];
+#pragma unroll
+    for (int kt = 0; kt < KTS; ++kt) s[kt] = f32x16{};
+    frag_t ka[2][KTS];
+    load_k(ka[0], Kb, 0);
+#pragma unroll
+    for (int kk = 0; kk < DK; ++kk) {
+      if (kk + 1 < DK) load_k(ka[(kk + 1) & 1], Kb, kk + 1);
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int kt = 0; kt < KTS; ++kt) {
-        s[kt] = f32x16{};
-        const int r = kt * 32 + l32;
-#pragma unroll
-        for (int kk = 0; kk < DK; ++kk) {
-          const uint8_t *src = &Ks[r * RB + k_unit<DT, D, BLK>(r, kk * 2 + half) * LB];
-          if constexpr (DT == kFP8) {
-            i32x8 a;
-            __builtin_memcpy(&a, src, 32);
-            s[kt] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, qf[kk], s[kt], 0, 0, 0, 127,
-                                                                    0, 127);
-          } else {
-            bf16x8 a;
-            __builtin_memcpy(&a, src, 16);
-            s[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[kk], s[kt], 0, 0, 0);
-          }
-        }
+        if constexpr (DT == kFP8)
+          s[kt] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(ka[kk & 1][kt], qf[kk], s[kt],
+                                                                  0, 0, 0, 127, 0, 127);
+        else
+          s[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[kk & 1][kt], qf[kk], s[kt], 0, 0, 0);
       }
-      // ---- online softmax, log2 domain.  Element r of tile kt is key
-      //      j0 + kt*32 + (r/4)*8 + half*4 + r%4 for query qi.
-      float mx = -INFINITY;
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    // V^T fragments of the first PV step load while the softmax runs
+    bf16x8 va[2][DTL];
+    load_v(va[0], Vb, 0);
+    if (diag) mask_diag(s, j0);
+    // ---- running max on raw scores; rescale only on a large increase
+    float mx = -INFINITY;
 #pragma unroll
-      for (int kt = 0; kt < KTS; ++kt)
+    for (int kt = 0; kt < KTS; ++kt)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          float x = s[kt][r] * scale2;
-          if (diag) {
-            const int key = j0 + kt * 32 + (r / 4) * 8 + half * 4 + (r % 4);
-            if (key > qi) x = -INFINITY;
-          }
-          s[kt][r] = x;
-          mx = fmaxf(mx, x);
-        }
-      mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-      const float mnew = fmaxf(m, mx);
-      const float msub = mnew == -INFINITY ? 0.f : mnew;
-      const float alpha = exp2f(m - msub);
+      for (int r = 0; r < 16; r += 2) mx = fmaxf(fmaxf(mx, s[kt][r]), s[kt][r + 1]);
+    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+    const float mx2 = mx * scale2;
+    if (__any(mx2 > m_used + kRescaleSlack)) {
+      const float mnew = fmaxf(m_used, mx2);
+      const float alpha = mnew == -INFINITY ? 1.f : __builtin_amdgcn_exp2f(m_used - mnew);
       l *= alpha;
 #pragma unroll
       for (int db = 0; db < DTL; ++db)
 #pragma unroll
         for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
-      m = mnew;
-      bf16x8 pb[KTS][2];
+      m_used = mnew;
+    }
+    const float mneg = m_used == -INFINITY ? 0.f : -m_used;
+    // ---- P = exp2(s * scale2 - m) packed to bf16 for the MFMA; the row sum
+    //      accumulates the fp32 values (two partial sums break the add chain)
+    bf16x8 pb[NJ];
+    float l0 = 0.f, l1 = 0.f;
 #pragma unroll
-      for (int kt = 0; kt < KTS; ++kt)
+    for (int j = 0; j < NJ; ++j) {
+      const int kt = j / 2, st = j % 2;
 #pragma unroll
-        for (int st = 0; st < 2; ++st)
+      for (int s8 = 0; s8 < 8; s8 += 2) {
+        const float p0 = __builtin_amdgcn_exp2f(fmaf(s[kt][st * 8 + s8], scale2, mneg));
+        const float p1 = __builtin_amdgcn_exp2f(fmaf(s[kt][st * 8 + s8 + 1], scale2, mneg));
+        l0 += p0;
+        l1 += p1;
+        pb[j][s8] = (__bf16)p0;
+        pb[j][s8 + 1] = (__bf16)p1;
+      }
+    }
+    l += l0 + l1;
+    // ---- O^T += V^T P^T.  Step j covers keys j*16 + [0,16); operand slot s of
+    //      lane half `half` is key j*16 + (s/4)*8 + half*4 + s%4 on both
+    //      operands.  The DTL accumulators alternate between MFMAs.
 #pragma unroll
-          for (int s8 = 0; s8 < 8; ++s8) {
-            const float p = exp2f(s[kt][st * 8 + s8] - msub);
-            l += p;
-            pb[kt][st][s8] = (__bf16)p;
-          }
-      // ---- O^T += V^T P^T.  Step (kt, st) covers keys kt*32 + st*16 + [0,16);
-      //      operand slot s of lane half `half` is key
-      //      kt*32 + st*16 + (s/4)*8 + half*4 + s%4 on both operands.
-      const int grp = lane >> 4, gi = lane & 15;
-      const int rr = gi >> 2, ss = gi & 3;
+    for (int j = 0; j < NJ; ++j) {
+      if (j + 1 < NJ) load_v(va[(j + 1) & 1], Vb, j + 1);
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-      for (int db = 0; db < DTL; ++db) {
-        const int dcol = db * 32 + (grp & 1) * 16 + ss * 4;
+      for (int db = 0; db < DTL; ++db)
+        oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[j & 1][db], pb[j], oacc[db], 0, 0, 0);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  }
+};
+
+template <int DT, int D, int BLK>
+__global__ __launch_bounds__(BLK * 2, 256 / BLK) void attn_mfma_kernel(
+    const uint8_t *__restrict__ q, const uint8_t *__restrict__ k, const uint8_t *__restrict__ v,
+    const int32_t *__restrict__ kv_idx, const int32_t *__restrict__ kv_cnt,
+    uint16_t *__restrict__ o, float *__restrict__ lse, const float *__restrict__ q_scale,
+    const float *__restrict__ k_scale, const float *__restrict__ v_scale, int hq, int hkv,
+    int seq, int nb, float sm_scale_log2, int xcd_map) {
+  using A = Attn<DT, D, BLK>;
+  using C = typename A::C;
+  constexpr int RB = C::RB, LB = C::LB, DK = C::DK, KT = C::KT, DTL = C::DTL, NSUB = C::NSUB;
+  __shared__ __attribute__((aligned(16))) uint8_t Ks0[C::KBYTES];
+  __shared__ __attribute__((aligned(16))) uint8_t Ks1[C::KBYTES];
+  __shared__ __attribute__((aligned(16))) uint16_t Vs0[KT * D];
+  __shared__ __attribute__((aligned(16))) uint16_t Vs1[KT * D];
+
+  A T;
+  const int tid = threadIdx.x;
+  T.lane = tid & 63;
+  T.w = tid >> 6;
+  T.half = T.lane >> 5;
+  T.l32 = T.lane & 31;
+  const int grp = hq / hkv;
+  int I, h;
+  {
+    const int bid = blockIdx.x;
+    if (xcd_map) {
+      // XCD x = bid % 8 serves kv group x % hkv; its workgroups walk the
+      // group's (row, head) items heaviest row first.
+      const int x = bid & 7, j = bid >> 3, X = 8 / hkv;
+      const int n = x / hkv + X * j;
+      I = nb - 1 - n / grp;
+      h = (x % hkv) * grp + n % grp;
+    } else {
+      I = nb - 1 - bid / hq;
+      h = bid % hq;
+    }
+  }
+  const int g = h / grp;
+  T.I = I;
+  T.seq = seq;
+  T.k = k;
+  T.v = v;
+  T.kvrow0 = (size_t)g * seq;
+  T.qi = I * BLK + T.w * 32 + T.l32;
+  const int half = T.half, qi = T.qi;
+  const size_t row = (size_t)h * nb + I;
+  T.scale2 = sm_scale_log2;
+  if constexpr (DT == kFP8) T.scale2 *= q_scale[h] * k_scale[g];
+  T.setup();
+
+  // Q fragments: B operand of S^T = K Q^T, query qi, LB bytes per step.
 #pragma unroll
-        for (int kt = 0; kt < KTS; ++kt)
+  for (int kk = 0; kk < DK; ++kk) {
+    const uint8_t *src = q + ((size_t)h * seq + min(qi, seq - 1)) * RB + kk * 2 * LB + half * LB;
+    uint4 a = *(const uint4 *)src, b = a;
+    if constexpr (LB == 32) b = *(const uint4 *)(src + 16);
+    if (qi >= seq) a = b = make_uint4(0, 0, 0, 0);
+    if constexpr (LB == 32) {
+      const uint4 ab[2] = {a, b};
+      __builtin_memcpy(&T.qf[kk], ab, 32);
+    } else {
+      __builtin_memcpy(&T.qf[kk], &a, 16);
+    }
+  }
 #pragma unroll
-          for (int st = 0; st < 2; ++st) {
-            const int r0 = kt * 32 + st * 16 + (grp >> 1) * 4 + rr;
-            const int r1 = r0 + 8;
-            const uint16_t *p0 = &Vs[r0 * D + v_chunk<D>(r0, dcol >> 3) * 8 + (dcol & 7)];
-            const uint16_t *p1 = &Vs[r1 * D + v_chunk<D>(r1, dcol >> 3) * 8 + (dcol & 7)];
-            const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4 *)p0);
-            const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4 *)p1);
-            const bf16x8 a = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-            oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[kt][st], oacc[db], 0, 0, 0);
-          }
+  for (int db = 0; db < DTL; ++db) T.oacc[db] = f32x16{};
+  T.m_used = -INFINITY;
+  T.l = 0.f;
+
+  const int nblk = kv_idx ? max(0, min(kv_cnt[row], nb)) : I + 1;
+  const int32_t *ilist = kv_idx ? kv_idx + row * nb : nullptr;
+  const int ns = nblk * NSUB;
+#define BSP_BLOCK_OF(t) (ilist ? ((ilist[t] < 0 || ilist[t] > I) ? -1 : ilist[t]) : (t))
+
+  // Pipeline: step i waits for sub-tile i (issued one step earlier), passes a
+  // barrier, issues sub-tile i+1 into the other buffer and computes i.  Block
+  // indices are read before the DMA is issued: vmcnt counts in order, so a
+  // later index load would also wait for the DMA.
+  int Jc = ns > 0 ? BSP_BLOCK_OF(0) : -1;
+  if (Jc >= 0) {
+    T.issue(Jc, 0, Ks0, Vs0);
+    if constexpr (DT == kFP8) T.store_v(Vs0);
+  }
+  for (int i = 0; i < ns; i += 2) {
+#pragma unroll
+    for (int ph = 0; ph < 2; ++ph) {
+      const int ii = i + ph;
+      if (ii < ns) {
+        const int Jn = ii + 1 < ns ? BSP_BLOCK_OF((ii + 1) / NSUB) : -1;
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        __syncthreads();
+        if (Jn >= 0) T.issue(Jn, (ii + 1) % NSUB, ph ? Ks0 : Ks1, ph ? Vs0 : Vs1);
+        if (Jc >= 0)
+          T.compute(ph ? Ks1 : Ks0, ph ? Vs1 : Vs0, Jc * BLK + (ii % NSUB) * KT, Jc == I);
+        if constexpr (DT == kFP8) {
+          if (Jn >= 0) T.store_v(ph ? Vs0 : Vs1);
+        }
+        Jc = Jn;
       }
     }
   }
+#undef BSP_BLOCK_OF
 
-  const float lt = l + __shfl_xor(l, 32, 64);
+  const float lt = T.l + __shfl_xor(T.l, 32, 64);
   if (qi < seq) {
     float inv = lt > 0.f ? 1.f / lt : 0.f;
     if constexpr (DT == kFP8) inv *= v_scale[g];
@@ -244,24 +427,25 @@ __global__ __launch_bounds__(BLK * 2) void attn_mfma_kernel(
       for (int gq = 0; gq < 4; ++gq) {
         const int d0 = db * 32 + gq * 8 + half * 4;
         uint2 pk;
-        pk.x = f32_to_bf16_bits(oacc[db][gq * 4 + 0] * inv) |
-               (f32_to_bf16_bits(oacc[db][gq * 4 + 1] * inv) << 16);
-        pk.y = f32_to_bf16_bits(oacc[db][gq * 4 + 2] * inv) |
-               (f32_to_bf16_bits(oacc[db][gq * 4 + 3] * inv) << 16);
+        pk.x = f32_to_bf16_bits(T.oacc[db][gq * 4 + 0] * inv) |
+               (f32_to_bf16_bits(T.oacc[db][gq * 4 + 1] * inv) << 16);
+        pk.y = f32_to_bf16_bits(T.oacc[db][gq * 4 + 2] * inv) |
+               (f32_to_bf16_bits(T.oacc[db][gq * 4 + 3] * inv) << 16);
         *(uint2 *)(orow + d0) = pk;
       }
     if (lse && half == 0)
-      lse[(size_t)h * seq + qi] = lt > 0.f ? (m + log2f(lt)) * kLn2 : -INFINITY;
+      lse[(size_t)h * seq + qi] = lt > 0.f ? (T.m_used + log2f(lt)) * kLn2 : -INFINITY;
   }
-  (void)ES;
 }
 
 template <int DT, int D, int BLK>
 static hipError_t launch_t(const Shape &s, const AttnArgs &a, hipStream_t st) {
-  hipLaunchKernelGGL((attn_mfma_kernel<DT, D, BLK>), dim3(s.hq * s.nb), dim3(BLK * 2), 0, st,
+  const long items = (long)s.hq * s.nb;
+  const int xcd = (s.hkv <= 8 && 8 % s.hkv == 0 && items % 8 == 0) ? 1 : 0;
+  hipLaunchKernelGGL((attn_mfma_kernel<DT, D, BLK>), dim3((unsigned)items), dim3(BLK * 2), 0, st,
                      (const uint8_t *)a.q, (const uint8_t *)a.k, (const uint8_t *)a.v, a.kv_idx,
                      a.kv_cnt, (uint16_t *)a.o, a.lse, a.q_scale, a.k_scale, a.v_scale, s.hq,
-                     s.hkv, s.seq, s.nb, a.sm_scale * kLog2e);
+                     s.hkv, s.seq, s.nb, a.sm_scale * kLog2e, xcd);
   return hipGetLastError();
 }
 
