@@ -242,6 +242,7 @@ struct Attn {
 #pragma unroll
     for (int kt = 0; kt < KTS; ++kt) s[kt] = f32x16{};
     frag_t ka[2][KTS];
+    __builtin_amdgcn_s_setprio(1);
     load_k(ka[0], Kb, 0);
 #pragma unroll
     for (int kk = 0; kk < DK; ++kk) {
@@ -257,6 +258,7 @@ struct Attn {
       }
       __builtin_amdgcn_sched_barrier(0);
     }
+    __builtin_amdgcn_s_setprio(0);
     // V^T fragments of the first PV step load while the softmax runs
     bf16x8 va[2][DTL];
     load_v(va[0], Vb, 0);
@@ -301,6 +303,7 @@ struct Attn {
     // ---- O^T += V^T P^T.  Step j covers keys j*16 + [0,16); operand slot s of
     //      lane half `half` is key j*16 + (s/4)*8 + half*4 + s%4 on both
     //      operands.  The DTL accumulators alternate between MFMAs.
+    __builtin_amdgcn_s_setprio(1);
 #pragma unroll
     for (int j = 0; j < NJ; ++j) {
       if (j + 1 < NJ) load_v(va[(j + 1) & 1], Vb, j + 1);
@@ -310,6 +313,7 @@ struct Attn {
         oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[j & 1][db], pb[j], oacc[db], 0, 0, 0);
       __builtin_amdgcn_sched_barrier(0);
     }
+    __builtin_amdgcn_s_setprio(0);
   }
 };
 
