@@ -5,9 +5,11 @@
 // retained on top; Appendix B: score, sink, window and causal masks are
 // combined, then the active-block indices are compressed).
 //
-// One wavefront per (head, query block) row.  The row maximum is a wavefront
-// max-reduction; the kept set is compacted into ascending order with a
-// 64-wide ballot and a popcount prefix per chunk of key blocks.
+// One wavefront per (head, query block) row; each lane covers 4 consecutive
+// key blocks per step (128-bit score loads).  The row maximum is a wavefront
+// max-reduction; the kept set is compacted in ascending order from four
+// 64-wide ballots per step: a lane's slot is the popcount of the kept bits of
+// lower lanes plus its own earlier kept elements.
 #include "device.h"
 #include "internal.h"
 
@@ -24,27 +26,83 @@ __global__ __launch_bounds__(256) void mask_kernel(const float *__restrict__ P,
   if (row >= rows) return;
   const int I = row % nb;
   const size_t off = (size_t)row * nb;
+  const bool vec = (nb & 3) == 0;  // rows are 16-byte aligned
+
+  auto load4 = [&](const float *p, int J, float (&x)[4]) {
+    if (vec && J + 3 < nb) {
+      const float4 t = *(const float4 *)(p + J);
+      x[0] = t.x; x[1] = t.y; x[2] = t.z; x[3] = t.w;
+    } else {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) x[e] = J + e < nb ? p[J + e] : 0.f;
+    }
+  };
+
   float thr = 0.f;
   if (!user) {
     float m = -INFINITY;
-    for (int J = lane; J <= I; J += 64) m = fmaxf(m, P[off + J]);
+    for (int J0 = 4 * lane; J0 <= I; J0 += 256) {
+      float x[4];
+      load4(P + off, J0, x);
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        if (J0 + e <= I) m = fmaxf(m, x[e]);
+    }
     thr = gamma * wave_max(m);
   }
+
   const uint64_t below = (1ull << lane) - 1ull;
   int n = 0;
-  for (int J0 = 0; J0 < nb; J0 += 64) {
-    const int J = J0 + lane;
-    bool keep = false;
+  for (int J0 = 0; J0 < nb; J0 += 256) {
+    const int J = J0 + 4 * lane;
+    bool keep[4] = {false, false, false, false};
     if (J <= I) {
-      if (user)
-        keep = user[off + J] != 0;
-      else
-        keep = P[off + J] >= thr || J < sink || I - J < local;
+      if (user) {
+        if (vec && J + 3 < nb) {
+          const uint32_t u4 = *(const uint32_t *)(user + off + J);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) keep[e] = ((u4 >> (8 * e)) & 0xFFu) != 0;
+        } else {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) keep[e] = J + e < nb && user[off + J + e] != 0;
+        }
+      } else {
+        float x[4];
+        load4(P + off, J, x);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int Je = J + e;
+          keep[e] = x[e] >= thr || Je < sink || I - Je < local;
+        }
+      }
+#pragma unroll
+      for (int e = 0; e < 4; ++e) keep[e] = keep[e] && J + e <= I;
     }
-    if (mask && J < nb) mask[off + J] = keep ? 1 : 0;
-    const uint64_t bal = __ballot(keep);
-    if (keep) kv_idx[off + n + __popcll(bal & below)] = J;
-    n += __popcll(bal);
+    if (mask) {
+      if (vec && J + 3 < nb) {
+        *(uint32_t *)(mask + off + J) = (uint32_t)keep[0] | ((uint32_t)keep[1] << 8) |
+                                        ((uint32_t)keep[2] << 16) | ((uint32_t)keep[3] << 24);
+      } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          if (J + e < nb) mask[off + J + e] = keep[e] ? 1 : 0;
+      }
+    }
+    uint64_t bal[4];
+    int before = 0, total = 0;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      bal[e] = __ballot(keep[e]);
+      before += __popcll(bal[e] & below);
+      total += __popcll(bal[e]);
+    }
+    int mine = 0;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      if (keep[e]) kv_idx[off + n + before + mine] = J + e;
+      mine += keep[e] ? 1 : 0;
+    }
+    n += total;
   }
   if (lane == 0) kv_cnt[row] = n;
 }

@@ -105,4 +105,12 @@ hipError_t launch_pool(const Shape &s, const void *q, const void *k, const float
   return launch_pool_dt<kFP8>(s, q, k, qs, ks, qp, kp, st);
 }
 
+// K only: the same kernel with no query heads in the grid.
+hipError_t launch_pool_k(const Shape &s, const void *k, const float *ks, float *kp,
+                         hipStream_t st) {
+  Shape t = s;
+  t.hq = 0;
+  return launch_pool(t, nullptr, k, nullptr, ks, nullptr, kp, st);
+}
+
 }  // namespace bsp

@@ -4,110 +4,203 @@
 // Appendix B: query tiles against causally valid pooled key blocks, then a
 // global normalisation).
 //
-//   score_logits_kernel   S[h][I][J] = c * q_pool[h][I] . k_pool[g][J], J <= I.
-//       A causal fp32 GEMM on the pooled operands.  One workgroup owns 64 query
-//       blocks of one head, keeps their pooled rows in LDS (d-major) and sweeps
-//       64-wide key-block tiles up to its diagonal; each lane accumulates a 4x4
-//       register tile.  fp32 throughout: the threshold compares scores, so the
-//       pooled operands are not rounded to a narrower type.
-//   score_softmax_kernel  one wavefront per row: max, sum of exp, normalise in
-//       place, zero the entries above the diagonal.
+// One kernel, two passes over the causal block grid of a group of 32 query
+// blocks:
+//   pass 1  S^T tiles = Kbar Qbar^T (32 key blocks x 32 query blocks) on
+//           v_mfma_f32_32x32x2_f32 - fp32 products and sums, so the
+//           threshold downstream sees full-precision scores - written out
+//           raw and reduced to the running row max and sum of exp;
+//   pass 2  each lane reads back the scores it wrote and normalises them in
+//           place, P = exp(S - max) / sum, with zeros above the diagonal.
+// Each lane owns one query block (a column of S^T), so the row
+// reductions are in-lane plus one exchange with the lane 32 away; the four
+// wavefronts of a workgroup split the key-block tiles of the same 32 query
+// blocks and merge their row statistics through LDS.  Groups are numbered
+// heaviest first.
 #include "device.h"
 #include "internal.h"
 
 namespace bsp {
 
-constexpr int kST = 64;  // query / key blocks per tile
-
 template <int D>
-__global__ __launch_bounds__(256) void score_logits_kernel(const float *__restrict__ q_pool,
-                                                           const float *__restrict__ k_pool,
-                                                           float *__restrict__ S, int hq, int hkv,
-                                                           int nb, float c) {
-  __shared__ float qt[D][kST + 4];
-  __shared__ float kt[D][kST + 4];
+__global__ __launch_bounds__(256) void score_kernel(const float *__restrict__ q_pool,
+                                                    const float *__restrict__ k_pool,
+                                                    float *__restrict__ P, int hq, int hkv, int nb,
+                                                    float c2) {
+  constexpr int KS = D / 2;  // k-steps; step ks, lane half h <-> dimension ks + KS*h
+  __shared__ float red_m[4][32], red_l[4][32];
+  __shared__ __attribute__((aligned(16))) float kt_s[4 * 32 * (D + 4)];
+  const int G = (nb + 31) / 32;
+  const int grp = G - 1 - (int)blockIdx.x;
   const int h = blockIdx.y;
   const int g = h / (hq / hkv);
-  const int I0 = blockIdx.x * kST;
-  const int tid = threadIdx.x;
-  const int ty = tid / 16, tx = tid % 16;
+  const int w = threadIdx.x >> 6, lane = threadIdx.x & 63, half = lane >> 5, l32 = lane & 31;
+  const int I0 = grp * 32;
+  const int Il = I0 + l32;  // this lane's query block
+  const bool row_ok = Il < nb;
+  const int ntc = (min(I0 + 31, nb - 1)) / 32 + 1;  // key-block tiles touching the causal part
 
-  constexpr int F4 = D / 4;  // float4 per pooled row
-  for (int e = tid; e < kST * F4; e += 256) {
-    const int r = e / F4, d4 = (e % F4) * 4;
-    float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
-    if (I0 + r < nb) v = *(const float4 *)(q_pool + ((size_t)h * nb + I0 + r) * D + d4);
-    qt[d4 + 0][r] = v.x;
-    qt[d4 + 1][r] = v.y;
-    qt[d4 + 2][r] = v.z;
-    qt[d4 + 3][r] = v.w;
+  // B operand (Qbar^T): lane holds Qbar[Il][ks + KS*half]
+  float qb[KS];
+  {
+    const float *src = q_pool + ((size_t)h * nb + min(Il, nb - 1)) * D + KS * half;
+#pragma unroll
+    for (int i = 0; i < KS; i += 4) {
+      const float4 t = *(const float4 *)(src + i);
+      qb[i] = row_ok ? t.x : 0.f;
+      qb[i + 1] = row_ok ? t.y : 0.f;
+      qb[i + 2] = row_ok ? t.z : 0.f;
+      qb[i + 3] = row_ok ? t.w : 0.f;
+    }
   }
-  const int Ilast = min(I0 + kST, nb) - 1;
-  for (int J0 = 0; J0 <= Ilast; J0 += kST) {
-    __syncthreads();
-    for (int e = tid; e < kST * F4; e += 256) {
-      const int r = e / F4, d4 = (e % F4) * 4;
-      float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
-      if (J0 + r < nb) v = *(const float4 *)(k_pool + ((size_t)g * nb + J0 + r) * D + d4);
-      kt[d4 + 0][r] = v.x;
-      kt[d4 + 1][r] = v.y;
-      kt[d4 + 2][r] = v.z;
-      kt[d4 + 3][r] = v.w;
+
+  // S^T tile jt: element r of the lane is key block J0 + (r/4)*8 + half*4 + r%4.
+  // The 32 Kbar rows of a tile are one contiguous block: each wave loads it
+  // with coalesced 16-byte loads one tile ahead, stores it to its own padded
+  // LDS slice (row stride D + 4 floats: conflict-free column reads) and reads
+  // the A operand (row l32, dimensions ks + KS*half) back from there.
+  constexpr int TF4 = 32 * D / 4 / 64;  // float4 per lane per tile
+  constexpr int RS = D + 4;             // padded LDS row stride (floats)
+  float *kt_lds = kt_s + w * 32 * RS;
+  typedef float4 stage_t[TF4];
+  auto fetch = [&](int jt, stage_t &st) {
+    const float *src = k_pool + ((size_t)g * nb + jt * 32) * D;
+    const int rows = min(32, nb - jt * 32);
+#pragma unroll
+    for (int i = 0; i < TF4; ++i) {
+      const int f = lane + 64 * i;  // float4 index inside the tile
+      st[i] = f / (D / 4) < rows ? *(const float4 *)(src + 4 * f) : make_float4(0.f, 0.f, 0.f, 0.f);
     }
-    __syncthreads();
-    float acc[4][4] = {};
-#pragma unroll 8
-    for (int d = 0; d < D; ++d) {
-      const float4 a = *(const float4 *)&qt[d][ty * 4];
-      const float4 b = *(const float4 *)&kt[d][tx * 4];
-      const float av[4] = {a.x, a.y, a.z, a.w};
-      const float bv[4] = {b.x, b.y, b.z, b.w};
+  };
+  auto stage = [&](const stage_t &st) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) acc[i][j] = fmaf(av[i], bv[j], acc[i][j]);
+    for (int i = 0; i < TF4; ++i) {
+      const int f = lane + 64 * i;
+      *(float4 *)(kt_lds + (f / (D / 4)) * RS + (f % (D / 4)) * 4) = st[i];
     }
+  };
+  auto mma = [&]() -> f32x16 {
+    const float *arow = kt_lds + l32 * RS + KS * half;
+    float4 a[KS / 4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int I = I0 + ty * 4 + i;
-      if (I >= nb) continue;
-      float *row = S + ((size_t)h * nb + I) * nb;
+    for (int i = 0; i < KS / 4; ++i) a[i] = *(const float4 *)(arow + 4 * i);
+    f32x16 acc = f32x16{};
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int J = J0 + tx * 4 + j;
-        if (J <= I) row[J] = acc[i][j] * c;
+    for (int i = 0; i < KS / 4; ++i) {
+      acc = __builtin_amdgcn_mfma_f32_32x32x2f32(a[i].x, qb[4 * i], acc, 0, 0, 0);
+      acc = __builtin_amdgcn_mfma_f32_32x32x2f32(a[i].y, qb[4 * i + 1], acc, 0, 0, 0);
+      acc = __builtin_amdgcn_mfma_f32_32x32x2f32(a[i].z, qb[4 * i + 2], acc, 0, 0, 0);
+      acc = __builtin_amdgcn_mfma_f32_32x32x2f32(a[i].w, qb[4 * i + 3], acc, 0, 0, 0);
+    }
+    return acc;
+  };
+
+  float *prow = P + ((size_t)h * nb + min(Il, nb - 1)) * nb;
+  const bool vec = (nb & 3) == 0;
+  // a lane's 16 values of tile jt are 4 runs of 4 consecutive key blocks
+  auto put_tile = [&](int jt, const float (&p)[16]) {
+#pragma unroll
+    for (int gq = 0; gq < 4; ++gq) {
+      const int J = jt * 32 + gq * 8 + half * 4;
+      if (vec && J + 3 < nb) {
+        *(float4 *)(prow + J) = make_float4(p[gq * 4], p[gq * 4 + 1], p[gq * 4 + 2], p[gq * 4 + 3]);
+      } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          if (J + e < nb) prow[J + e] = p[gq * 4 + e];
       }
     }
-  }
-}
+  };
+  auto get_tile = [&](int jt, float (&p)[16]) {
+#pragma unroll
+    for (int gq = 0; gq < 4; ++gq) {
+      const int J = jt * 32 + gq * 8 + half * 4;
+      if (vec && J + 3 < nb) {
+        const float4 t = *(const float4 *)(prow + J);
+        p[gq * 4] = t.x; p[gq * 4 + 1] = t.y; p[gq * 4 + 2] = t.z; p[gq * 4 + 3] = t.w;
+      } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) p[gq * 4 + e] = J + e < nb ? prow[J + e] : 0.f;
+      }
+    }
+  };
 
-__global__ __launch_bounds__(256) void score_softmax_kernel(float *__restrict__ S, int rows,
-                                                            int nb) {
-  const int lane = threadIdx.x & 63;
-  const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (row >= rows) return;
-  const int I = row % nb;
-  float *p = S + (size_t)row * nb;
-  float m = -INFINITY;
-  for (int J = lane; J <= I; J += 64) m = fmaxf(m, p[J]);
-  m = wave_max(m);
-  float l = 0.f;
-  for (int J = lane; J <= I; J += 64) l += expf(p[J] - m);
-  l = wave_sum(l);
-  const float inv = 1.f / l;
-  for (int J = lane; J < nb; J += 64) p[J] = J <= I ? expf(p[J] - m) * inv : 0.f;
+  // ---- pass 1: row max and sum of exp2 (log2 domain)
+  float m = -INFINITY, l = 0.f;
+  stage_t nxt;
+  if (w < ntc) fetch(w, nxt);
+  for (int jt = w; jt < ntc; jt += 4) {
+    stage(nxt);
+    if (jt + 4 < ntc) fetch(jt + 4, nxt);
+    const f32x16 acc = mma();
+    float s[16];
+    float tmax = -INFINITY;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int J = jt * 32 + (r / 4) * 8 + half * 4 + (r % 4);
+      s[r] = (J <= Il && J < nb) ? acc[r] * c2 : -INFINITY;
+      tmax = fmaxf(tmax, s[r]);
+    }
+    if (row_ok) put_tile(jt, s);  // raw log2-domain scores, normalised in pass 2
+    const float mn = fmaxf(m, tmax);
+    if (mn != -INFINITY) {
+      float acc_l = 0.f;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc_l += exp2f(s[r] - mn);
+      l = l * exp2f(m - mn) + acc_l;
+      m = mn;
+    }
+  }
+  // merge the two lane halves, then the four wavefronts
+  {
+    const float mo = __shfl_xor(m, 32, 64), lo = __shfl_xor(l, 32, 64);
+    const float mn = fmaxf(m, mo);
+    if (mn != -INFINITY) {
+      l = (m == -INFINITY ? 0.f : l * exp2f(m - mn)) + (mo == -INFINITY ? 0.f : lo * exp2f(mo - mn));
+      m = mn;
+    }
+  }
+  if (half == 0) {
+    red_m[w][l32] = m;
+    red_l[w][l32] = l;
+  }
+  __syncthreads();
+  float M = -INFINITY;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) M = fmaxf(M, red_m[i][l32]);
+  float L = 0.f;
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+    if (red_m[i][l32] != -INFINITY) L += red_l[i][l32] * exp2f(red_m[i][l32] - M);
+  const float invL = L > 0.f ? 1.f / L : 0.f;
+
+  // ---- pass 2: P = exp2(s - M) / L from the stored scores, zeros above.
+  // Each lane re-reads exactly the values it wrote, so no barrier is needed.
+  if (!row_ok) return;
+  const int ntall = (nb + 31) / 32;
+  for (int jt = w; jt < ntall; jt += 4) {
+    float p[16];
+    if (jt < ntc) {
+      get_tile(jt, p);
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int J = jt * 32 + (r / 4) * 8 + half * 4 + (r % 4);
+        p[r] = (J <= Il) ? exp2f(p[r] - M) * invL : 0.f;
+      }
+    } else {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) p[r] = 0.f;
+    }
+    put_tile(jt, p);
+  }
 }
 
 template <int D>
 static hipError_t launch_score_t(const Shape &s, float c, const float *qp, const float *kp,
                                  float *S, hipStream_t st) {
-  dim3 grid((s.nb + kST - 1) / kST, s.hq);
-  hipLaunchKernelGGL(score_logits_kernel<D>, grid, dim3(256), 0, st, qp, kp, S, s.hq, s.hkv,
-                     s.nb, c);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  const int rows = s.hq * s.nb;
-  hipLaunchKernelGGL(score_softmax_kernel, dim3((rows + 3) / 4), dim3(256), 0, st, S, rows, s.nb);
+  dim3 grid((s.nb + 31) / 32, s.hq);
+  hipLaunchKernelGGL(score_kernel<D>, grid, dim3(256), 0, st, qp, kp, S, s.hq, s.hkv, s.nb,
+                     c * kLog2e);
   return hipGetLastError();
 }
 
