@@ -50,6 +50,8 @@ def parse():
     p.add_argument("--seq", type=int, default=None, help="override sequence length")
     p.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     p.add_argument("--cpu-rows", type=int, default=8192, help="query rows in the CPU sample")
+    p.add_argument("--s2", action="store_true",
+                   help="planted strengths scaled by d**0.25 (logit units): the threshold prunes")
     p.add_argument("--user-density", type=float, default=None,
                    help="replace the scorer by a random caller mask of this density")
     p.add_argument("--copy-calibration", action="store_true",
@@ -138,7 +140,7 @@ def main():
     assert torch.cuda.is_available(), "needs a GPU"
     torch.cuda.set_device(0)
 
-    c = gen.make_config(a.config, seq=a.seq)
+    c = gen.make_s2(a.config, seq=a.seq) if a.s2 else gen.make_config(a.config, seq=a.seq)
     hq, hkv, seq, d, B = c.hq, c.hkv, c.seq, c.d, c.block
     nb = c.nb
 
@@ -221,11 +223,14 @@ def main():
     if not a.no_cpu:
         cpu = cpu_baseline(c, mk.cpu().numpy(), a.cpu_rows)
 
-    traffic = traffic_from_note() if (a.config == 3 and a.seq is None and um is None) else None
+    traffic = traffic_from_note() if (a.config == 3 and a.seq is None and um is None
+                                      and not a.s2) else None
     wl = (f"{c.name}: {hq} q / {hkv} kv heads, seq {seq}, d {d}, block {B}, gamma {c.gamma}, "
           f"causal, {c.dtype}, batch 1, one layer")
     if um is not None:
         wl += f", caller mask density {a.user_density}"
+    if a.s2:
+        wl += ", planted strengths in logit units (x d^0.25)"
     out = {
         "metric": "sparse prefill-attn ms/layer + effective TFLOP/s at 128K bf16; % MFMA peak",
         "value": round(F_dense / (ms_step * 1e-3) / 1e12, 3),

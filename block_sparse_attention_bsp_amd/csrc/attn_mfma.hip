@@ -85,11 +85,7 @@ __device__ __forceinline__ int v_chunk(int r, int c) {
   return c ^ (((r / VRPW) % NG) << 2);
 }
 
-__device__ __forceinline__ uint32_t e4m3_pair_to_bf16(uint32_t two) {
-  // two e4m3 codes (low byte first) -> two bf16 (exact: 4 significant bits)
-  return (__float_as_uint(e4m3_to_f32(two & 0xFFu)) >> 16) |
-         (__float_as_uint(e4m3_to_f32((two >> 8) & 0xFFu)) & 0xFFFF0000u);
-}
+
 
 __device__ __forceinline__ void lds_dma16(const void *gsrc, void *ldst) {
   __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void *)gsrc,
@@ -194,10 +190,10 @@ struct Attn {
         const int e = threadIdx.x + it * NT;
         const int r = e / (RB / 16), c = e % (RB / 16);
         const uint4 vv4 = vreg[it];
-        const uint4 lo = make_uint4(e4m3_pair_to_bf16(vv4.x), e4m3_pair_to_bf16(vv4.x >> 16),
-                                    e4m3_pair_to_bf16(vv4.y), e4m3_pair_to_bf16(vv4.y >> 16));
-        const uint4 hi = make_uint4(e4m3_pair_to_bf16(vv4.z), e4m3_pair_to_bf16(vv4.z >> 16),
-                                    e4m3_pair_to_bf16(vv4.w), e4m3_pair_to_bf16(vv4.w >> 16));
+        const uint4 lo = make_uint4(e4m3x2_to_bf16x2(vv4.x, false), e4m3x2_to_bf16x2(vv4.x, true),
+                                    e4m3x2_to_bf16x2(vv4.y, false), e4m3x2_to_bf16x2(vv4.y, true));
+        const uint4 hi = make_uint4(e4m3x2_to_bf16x2(vv4.z, false), e4m3x2_to_bf16x2(vv4.z, true),
+                                    e4m3x2_to_bf16x2(vv4.w, false), e4m3x2_to_bf16x2(vv4.w, true));
         *(uint4 *)&Vb[r * D + v_chunk<D>(r, 2 * c) * 8] = lo;
         *(uint4 *)&Vb[r * D + v_chunk<D>(r, 2 * c + 1) * 8] = hi;
       }

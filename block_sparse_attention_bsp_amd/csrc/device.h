@@ -38,6 +38,23 @@ __device__ __forceinline__ float e4m3_to_f32(uint32_t c) {
   return __uint_as_float(__float_as_uint(v) | s);
 }
 
+// Two OCP e4m3fn codes (bytes 0-1 of w if !hi, bytes 2-3 if hi) -> two
+// floats / two bf16 (both exact: e4m3 has 4 significant bits), on the gfx950
+// conversion units.
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ f32x2 e4m3x2_to_f32(uint32_t w, bool hi) {
+  return hi ? __builtin_amdgcn_cvt_pk_f32_fp8((int)w, true)
+            : __builtin_amdgcn_cvt_pk_f32_fp8((int)w, false);
+}
+__device__ __forceinline__ uint32_t e4m3x2_to_bf16x2(uint32_t w, bool hi) {
+  const bf16x2 r = hi ? __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)w, 1.0f, true)
+                      : __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)w, 1.0f, false);
+  uint32_t u;
+  __builtin_memcpy(&u, &r, 4);
+  return u;
+}
+
 // float -> bfloat16 bits, round to nearest even (finite inputs).
 __device__ __forceinline__ uint32_t f32_to_bf16_bits(float x) {
   uint32_t u = __float_as_uint(x);

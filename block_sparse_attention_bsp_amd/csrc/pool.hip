@@ -59,8 +59,11 @@ __global__ __launch_bounds__(256) void pool_kernel(const uint8_t *__restrict__ q
         acc[2 * j] += bf16_bits_to_f32(wd[j] & 0xFFFFu);
         acc[2 * j + 1] += bf16_bits_to_f32(wd[j] >> 16);
       } else {
-#pragma unroll
-        for (int b = 0; b < 4; ++b) acc[4 * j + b] += e4m3_to_f32((wd[j] >> (8 * b)) & 0xFFu);
+        const f32x2 lo = e4m3x2_to_f32(wd[j], false), hi = e4m3x2_to_f32(wd[j], true);
+        acc[4 * j] += lo.x;
+        acc[4 * j + 1] += lo.y;
+        acc[4 * j + 2] += hi.x;
+        acc[4 * j + 3] += hi.y;
       }
     }
   }
