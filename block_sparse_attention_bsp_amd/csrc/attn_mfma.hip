@@ -385,13 +385,31 @@ __global__ __launch_bounds__(BLK * 2, 256 / BLK) void attn_mfma_kernel(
   const int nblk = kv_idx ? max(0, min(kv_cnt[row], nb)) : I + 1;
   const int32_t *ilist = kv_idx ? kv_idx + row * nb : nullptr;
   const int ns = nblk * NSUB;
-#define BSP_BLOCK_OF(t) (ilist ? ((ilist[t] < 0 || ilist[t] > I) ? -1 : ilist[t]) : (t))
+  // The kv list streams through registers 64 entries at a time: lane l holds
+  // entry 64c + l of chunk c, and chunk c + 1 is loaded on entering chunk c.
+  // An entry is picked with readlane, so no step waits on a global load of
+  // its block index (such waits desynchronise the workgroups that otherwise
+  // walk the same K/V blocks together out of L2).  Invalid entries are skipped.
+  int lcur = 0, lnxt = 0, chunk = 0;
+  if (ilist) {
+    lcur = T.lane < nblk ? ilist[T.lane] : 0;
+    lnxt = 64 + T.lane < nblk ? ilist[64 + T.lane] : 0;
+  }
+  auto block_of = [&](int t) -> int {
+    if (!ilist) return t;
+    if ((t >> 6) != chunk) {  // t grows by at most one per call
+      chunk = t >> 6;
+      lcur = lnxt;
+      const int e = (chunk + 1) * 64 + T.lane;
+      lnxt = e < nblk ? ilist[e] : 0;
+    }
+    const int J = __builtin_amdgcn_readlane(lcur, t & 63);
+    return (J < 0 || J > I) ? -1 : J;
+  };
 
   // Pipeline: step i waits for sub-tile i (issued one step earlier), passes a
-  // barrier, issues sub-tile i+1 into the other buffer and computes i.  Block
-  // indices are read before the DMA is issued: vmcnt counts in order, so a
-  // later index load would also wait for the DMA.
-  int Jc = ns > 0 ? BSP_BLOCK_OF(0) : -1;
+  // barrier, issues sub-tile i+1 into the other buffer and computes i.
+  int Jc = ns > 0 ? block_of(0) : -1;
   if (Jc >= 0) {
     T.issue(Jc, 0, Ks0, Vs0);
     if constexpr (DT == kFP8) T.store_v(Vs0);
@@ -401,7 +419,7 @@ __global__ __launch_bounds__(BLK * 2, 256 / BLK) void attn_mfma_kernel(
     for (int ph = 0; ph < 2; ++ph) {
       const int ii = i + ph;
       if (ii < ns) {
-        const int Jn = ii + 1 < ns ? BSP_BLOCK_OF((ii + 1) / NSUB) : -1;
+        const int Jn = ii + 1 < ns ? block_of((ii + 1) / NSUB) : -1;
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         __syncthreads();
         if (Jn >= 0) T.issue(Jn, (ii + 1) % NSUB, ph ? Ks0 : Ks1, ph ? Vs0 : Vs1);
@@ -414,7 +432,6 @@ __global__ __launch_bounds__(BLK * 2, 256 / BLK) void attn_mfma_kernel(
       }
     }
   }
-#undef BSP_BLOCK_OF
 
   const float lt = T.l + __shfl_xor(T.l, 32, 64);
   if (qi < seq) {

@@ -138,8 +138,10 @@ bsp_status bsp_mask(const bsp_desc *desc, const float *score, const uint8_t *use
  * blocks listed in kv_idx[h][I][0 .. kv_cnt[h][I]) with j <= i:
  *   o[h][i][:] = sum_j softmax_j(c * q_i . k_j) * v_j[:]
  *   lse[h][i]  = ln sum_j exp(c * q_i . k_j)      (natural log)
- * An empty set gives o = 0 and lse = -inf.  Block indices must be distinct,
- * in [0, I]; the order of a row does not change the result beyond rounding.
+ * An empty set gives o = 0 and lse = -inf.  Block indices must be distinct;
+ * entries outside [0, I] are skipped and kv_cnt is clamped to [0, nb], so a
+ * malformed list never reads out of bounds.  The order of a row does not
+ * change the result beyond rounding.
  *
  * q, k, v:  device, storage dtype; fp8 needs all three desc scales
  * kv_idx, kv_cnt: device, as produced by bsp_mask; both NULL = dense causal

@@ -83,6 +83,51 @@ def test_config_shape_4k_sampled(dtype):
     full_check(c, rows=rows)
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "fp8"])
+def test_long_kv_lists(dtype):
+    """Rows whose kv lists are long enough to span several 64-entry chunks:
+    exact counts around 64 and 128, random rows, and lists padded with
+    entries outside [0, I] that must be skipped."""
+    announce(f"long kv lists {dtype}")
+    c = gen.make_case(2, 1, 260 * 64, 64, 64, dtype, 77, rope=True, n_vert=4)
+    nb = c.nb
+    rng = np.random.default_rng(3)
+    m = (rng.random((2, nb, nb)) < 0.6).astype(np.uint8) & np.tril(np.ones((nb, nb), np.uint8))
+    special = {200: 63, 201: 64, 202: 65, 203: 127, 204: 128, 205: 129, 259: 130}
+    for I, kk in special.items():
+        m[0, I, :] = 0
+        m[0, I, :kk] = 1
+    idx, cnt = H.idx_from_mask(m)
+    # head 1, rows 100..139: two entries the kernel must skip, at random places
+    bad = idx.copy()
+    bcnt = cnt.copy()
+    for I in range(100, 140):
+        lst = list(bad[1, I, :bcnt[1, I]])
+        for x in (-1, I + 1 + int(rng.integers(0, nb - I - 1))):
+            lst.insert(int(rng.integers(0, len(lst) + 1)), x)
+        bad[1, I, :len(lst)] = lst
+        bcnt[1, I] = len(lst)
+    d = H.dev(c)
+    kw = dict(q_scale=d["q_scale"], k_scale=d["k_scale"], v_scale=d["v_scale"])
+    o, lse = bsp.attn_fwd(d["q"], d["k"], d["v"], c.block, torch.from_numpy(idx).cuda(),
+                          torch.from_numpy(cnt).cuda(), **kw)
+    o2, lse2 = bsp.attn_fwd(d["q"], d["k"], d["v"], c.block, torch.from_numpy(bad).cuda(),
+                            torch.from_numpy(bcnt).cuda(), **kw)
+    torch.cuda.synchronize()
+    assert torch.equal(o, o2) and torch.equal(lse, lse2)
+    B = c.block
+    pos = [I * B + t for I in special for t in (0, 17, B - 1)]
+    pos += [I * B + t for I in (100, 120, 139) for t in (0, B - 1)]
+    pos += rng.integers(0, c.seq, 24).tolist()
+    pos = np.array(sorted(set(pos)), np.int64)
+    rows = np.concatenate([pos, c.seq + pos])
+    oo, ol = oracle.attn(c.q, c.k, c.v, dtype, B, m, q_scale=c.q_scale, k_scale=c.k_scale,
+                         v_scale=c.v_scale, rows=rows)
+    go, gl = H.gather_rows(o, lse, rows)
+    err = H.check_attn(go, gl, oo, ol, dtype)
+    print(f"  max-abs O err {err:.2e}", flush=True)
+
+
 def test_gamma0_equals_dense_path_bitwise():
     announce("gamma=0 vs dense")
     c = gen.make_case(4, 2, 1024, 128, 128, "bf16", 5, rope=True, n_vert=4)
