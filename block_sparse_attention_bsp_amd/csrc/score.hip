@@ -8,15 +8,17 @@
 // blocks:
 //   pass 1  S^T tiles = Kbar Qbar^T (32 key blocks x 32 query blocks) on
 //           v_mfma_f32_32x32x2_f32 - fp32 products and sums, so the
-//           threshold downstream sees full-precision scores - written out
-//           raw and reduced to the running row max and sum of exp;
-//   pass 2  each lane reads back the scores it wrote and normalises them in
-//           place, P = exp(S - max) / sum, with zeros above the diagonal.
+//           threshold downstream sees full-precision scores - reduced to the
+//           running row max and sum of exp and written out raw, transposed
+//           through LDS so that every store covers whole 128-byte row runs;
+//   pass 2  after a barrier the workgroup sweeps its 32 rows of P row-major
+//           with 16-byte accesses: P = exp(S - max) / sum from the raw
+//           scores on the causal part, zeros above it.
 // Each lane owns one query block (a column of S^T), so the row
 // reductions are in-lane plus one exchange with the lane 32 away; the four
 // wavefronts of a workgroup split the key-block tiles of the same 32 query
-// blocks and merge their row statistics through LDS.  Groups are numbered
-// heaviest first.
+// blocks and merge their row statistics through LDS.  The grid launches the
+// heaviest row groups of every head first.
 #include "device.h"
 #include "internal.h"
 
@@ -28,17 +30,20 @@ __global__ __launch_bounds__(256) void score_kernel(const float *__restrict__ q_
                                                     float *__restrict__ P, int hq, int hkv, int nb,
                                                     float c2) {
   constexpr int KS = D / 2;  // k-steps; step ks, lane half h <-> dimension ks + KS*h
-  __shared__ float red_m[4][32], red_l[4][32];
+  __shared__ float red_m[4][32], red_l[4][32], row_m[32], row_inv[32];
   __shared__ __attribute__((aligned(16))) float kt_s[4 * 32 * (D + 4)];
   const int G = (nb + 31) / 32;
-  const int grp = G - 1 - (int)blockIdx.x;
-  const int h = blockIdx.y;
+  const int grp = G - 1 - (int)blockIdx.y;
+  const int h = blockIdx.x;
   const int g = h / (hq / hkv);
   const int w = threadIdx.x >> 6, lane = threadIdx.x & 63, half = lane >> 5, l32 = lane & 31;
   const int I0 = grp * 32;
+  const int rows = min(32, nb - I0);
   const int Il = I0 + l32;  // this lane's query block
-  const bool row_ok = Il < nb;
-  const int ntc = (min(I0 + 31, nb - 1)) / 32 + 1;  // key-block tiles touching the causal part
+  const bool row_ok = l32 < rows;
+  const int ntc = (I0 + rows - 1) / 32 + 1;  // key-block tiles touching the causal part
+  const bool vec = (nb & 3) == 0;             // rows of P are 16-byte aligned
+  float *pgrp = P + ((size_t)h * nb + I0) * nb;
 
   // B operand (Qbar^T): lane holds Qbar[Il][ks + KS*half]
   float qb[KS];
@@ -58,18 +63,20 @@ __global__ __launch_bounds__(256) void score_kernel(const float *__restrict__ q_
   // The 32 Kbar rows of a tile are one contiguous block: each wave loads it
   // with coalesced 16-byte loads one tile ahead, stores it to its own padded
   // LDS slice (row stride D + 4 floats: conflict-free column reads) and reads
-  // the A operand (row l32, dimensions ks + KS*half) back from there.
+  // the A operand (row l32, dimensions ks + KS*half) back from there.  The
+  // same slice then carries the tile's transpose for row-contiguous stores.
   constexpr int TF4 = 32 * D / 4 / 64;  // float4 per lane per tile
   constexpr int RS = D + 4;             // padded LDS row stride (floats)
+  constexpr int TS = 33;                // transpose row stride (floats)
   float *kt_lds = kt_s + w * 32 * RS;
   typedef float4 stage_t[TF4];
   auto fetch = [&](int jt, stage_t &st) {
     const float *src = k_pool + ((size_t)g * nb + jt * 32) * D;
-    const int rows = min(32, nb - jt * 32);
+    const int n = min(32, nb - jt * 32);
 #pragma unroll
     for (int i = 0; i < TF4; ++i) {
       const int f = lane + 64 * i;  // float4 index inside the tile
-      st[i] = f / (D / 4) < rows ? *(const float4 *)(src + 4 * f) : make_float4(0.f, 0.f, 0.f, 0.f);
+      st[i] = f / (D / 4) < n ? *(const float4 *)(src + 4 * f) : make_float4(0.f, 0.f, 0.f, 0.f);
     }
   };
   auto stage = [&](const stage_t &st) {
@@ -94,38 +101,31 @@ __global__ __launch_bounds__(256) void score_kernel(const float *__restrict__ q_
     }
     return acc;
   };
-
-  float *prow = P + ((size_t)h * nb + min(Il, nb - 1)) * nb;
-  const bool vec = (nb & 3) == 0;
-  // a lane's 16 values of tile jt are 4 runs of 4 consecutive key blocks
-  auto put_tile = [&](int jt, const float (&p)[16]) {
+  // Raw scores of tile jt -> P through the wave's LDS slice: written by
+  // (row, key) = (l32, r), read back so that 8 lanes cover one row's 32 keys.
+  auto put_tile = [&](int jt, const float (&s)[16]) {
 #pragma unroll
-    for (int gq = 0; gq < 4; ++gq) {
-      const int J = jt * 32 + gq * 8 + half * 4;
-      if (vec && J + 3 < nb) {
-        *(float4 *)(prow + J) = make_float4(p[gq * 4], p[gq * 4 + 1], p[gq * 4 + 2], p[gq * 4 + 3]);
-      } else {
+    for (int r = 0; r < 16; ++r) kt_lds[l32 * TS + (r / 4) * 8 + half * 4 + (r % 4)] = s[r];
+    const int c4 = (lane & 7) * 4;
 #pragma unroll
-        for (int e = 0; e < 4; ++e)
-          if (J + e < nb) prow[J + e] = p[gq * 4 + e];
-      }
-    }
-  };
-  auto get_tile = [&](int jt, float (&p)[16]) {
+    for (int it = 0; it < 4; ++it) {
+      const int rr = it * 8 + (lane >> 3);
+      const float *t = kt_lds + rr * TS + c4;
+      const int J = jt * 32 + c4;
+      float *dst = pgrp + (size_t)rr * nb + J;
+      if (rr < rows) {
+        if (vec && J + 3 < nb) {
+          *(float4 *)dst = make_float4(t[0], t[1], t[2], t[3]);
+        } else {
 #pragma unroll
-    for (int gq = 0; gq < 4; ++gq) {
-      const int J = jt * 32 + gq * 8 + half * 4;
-      if (vec && J + 3 < nb) {
-        const float4 t = *(const float4 *)(prow + J);
-        p[gq * 4] = t.x; p[gq * 4 + 1] = t.y; p[gq * 4 + 2] = t.z; p[gq * 4 + 3] = t.w;
-      } else {
-#pragma unroll
-        for (int e = 0; e < 4; ++e) p[gq * 4 + e] = J + e < nb ? prow[J + e] : 0.f;
+          for (int e = 0; e < 4; ++e)
+            if (J + e < nb) dst[e] = t[e];
+        }
       }
     }
   };
 
-  // ---- pass 1: row max and sum of exp2 (log2 domain)
+  // ---- pass 1: raw log2-domain scores to P, row max and sum of exp2
   float m = -INFINITY, l = 0.f;
   stage_t nxt;
   if (w < ntc) fetch(w, nxt);
@@ -141,7 +141,7 @@ __global__ __launch_bounds__(256) void score_kernel(const float *__restrict__ q_
       s[r] = (J <= Il && J < nb) ? acc[r] * c2 : -INFINITY;
       tmax = fmaxf(tmax, s[r]);
     }
-    if (row_ok) put_tile(jt, s);  // raw log2-domain scores, normalised in pass 2
+    put_tile(jt, s);
     const float mn = fmaxf(m, tmax);
     if (mn != -INFINITY) {
       float acc_l = 0.f;
@@ -165,40 +165,64 @@ __global__ __launch_bounds__(256) void score_kernel(const float *__restrict__ q_
     red_l[w][l32] = l;
   }
   __syncthreads();
-  float M = -INFINITY;
+  if (w == 0 && half == 0) {
+    float M = -INFINITY;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) M = fmaxf(M, red_m[i][l32]);
-  float L = 0.f;
+    for (int i = 0; i < 4; ++i) M = fmaxf(M, red_m[i][l32]);
+    float L = 0.f;
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
-    if (red_m[i][l32] != -INFINITY) L += red_l[i][l32] * exp2f(red_m[i][l32] - M);
-  const float invL = L > 0.f ? 1.f / L : 0.f;
+    for (int i = 0; i < 4; ++i)
+      if (red_m[i][l32] != -INFINITY) L += red_l[i][l32] * exp2f(red_m[i][l32] - M);
+    row_m[l32] = M;
+    row_inv[l32] = L > 0.f ? 1.f / L : 0.f;
+  }
+  __syncthreads();
 
-  // ---- pass 2: P = exp2(s - M) / L from the stored scores, zeros above.
-  // Each lane re-reads exactly the values it wrote, so no barrier is needed.
-  if (!row_ok) return;
-  const int ntall = (nb + 31) / 32;
-  for (int jt = w; jt < ntall; jt += 4) {
-    float p[16];
-    if (jt < ntc) {
-      get_tile(jt, p);
+  // ---- pass 2: the group's rows of P, row-major and coalesced: causal
+  // entries become exp2(s - M) / L from the raw scores of pass 1, the rest 0.
+  const int jend = ntc * 32;  // raw scores exist for J < jend (-inf above the diagonal)
+  if (vec) {
+    // 8 rows per batch: all loads are issued before the first store
+    for (int J = threadIdx.x * 4; J < nb; J += 1024) {
+      for (int r0 = 0; r0 < rows; r0 += 8) {
+        float4 v[8];
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int J = jt * 32 + (r / 4) * 8 + half * 4 + (r % 4);
-        p[r] = (J <= Il) ? exp2f(p[r] - M) * invL : 0.f;
+        for (int u = 0; u < 8; ++u) {
+          const int rr = r0 + u;
+          v[u] = (rr < rows && J < jend) ? *(const float4 *)(pgrp + (size_t)rr * nb + J)
+                                         : make_float4(0.f, 0.f, 0.f, 0.f);
+        }
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          const int rr = r0 + u;
+          if (rr < rows) {
+            if (J < jend) {
+              const float M = row_m[rr], inv = row_inv[rr];
+              v[u].x = exp2f(v[u].x - M) * inv;
+              v[u].y = exp2f(v[u].y - M) * inv;
+              v[u].z = exp2f(v[u].z - M) * inv;
+              v[u].w = exp2f(v[u].w - M) * inv;
+            }
+            *(float4 *)(pgrp + (size_t)rr * nb + J) = v[u];
+          }
+        }
       }
-    } else {
-#pragma unroll
-      for (int r = 0; r < 16; ++r) p[r] = 0.f;
     }
-    put_tile(jt, p);
+  } else {
+    for (int rr = 0; rr < rows; ++rr) {
+      const float M = row_m[rr], inv = row_inv[rr];
+      float *prow = pgrp + (size_t)rr * nb;
+      for (int J = threadIdx.x; J < nb; J += 256)
+        prow[J] = J < jend ? exp2f(prow[J] - M) * inv : 0.f;
+    }
   }
 }
 
 template <int D>
 static hipError_t launch_score_t(const Shape &s, float c, const float *qp, const float *kp,
                                  float *S, hipStream_t st) {
-  dim3 grid((s.nb + 31) / 32, s.hq);
+  // heaviest row groups of every head first
+  dim3 grid(s.hq, (s.nb + 31) / 32);
   hipLaunchKernelGGL(score_kernel<D>, grid, dim3(256), 0, st, qp, kp, S, s.hq, s.hkv, s.nb,
                      c * kLog2e);
   return hipGetLastError();
