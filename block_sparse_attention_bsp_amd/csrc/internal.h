@@ -22,8 +22,6 @@ struct AttnArgs {
 
 hipError_t launch_pool(const Shape &s, const void *q, const void *k, const float *q_scale,
                        const float *k_scale, float *q_pool, float *k_pool, hipStream_t st);
-hipError_t launch_pool_k(const Shape &s, const void *k, const float *k_scale, float *k_pool,
-                         hipStream_t st);
 hipError_t launch_score(const Shape &s, float c, const float *q_pool, const float *k_pool,
                         float *score, hipStream_t st);
 hipError_t launch_mask(const Shape &s, float gamma, int sink_blocks, int local_blocks,
