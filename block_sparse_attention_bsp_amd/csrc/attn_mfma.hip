@@ -22,10 +22,11 @@
 //     accumulator of a lane belongs to its own query.  P^T is the B operand
 //     straight from the score registers; the key order inside a 16-key step is
 //     permuted identically on both operands.
-//   * K/V sub-tiles of 64 keys are double-buffered in LDS and filled by
-//     global_load_lds_dwordx4 (no VGPR staging) one sub-tile ahead, so the
-//     load of sub-tile i+1 overlaps the MFMAs of sub-tile i; one barrier per
-//     sub-tile.  K rows carry an XOR swizzle of their read units; V is stored
+//   * K/V sub-tiles of 64 keys are double-buffered in LDS and filled one
+//     sub-tile ahead by buffer_load_dwordx4 ... lds (no VGPR staging; one
+//     buffer descriptor per kv head, the sub-tile position as the scalar
+//     offset, loop-invariant lane offsets), so the load of sub-tile i+1
+//     overlaps the MFMAs of sub-tile i; one barrier per sub-tile.  K rows carry an XOR swizzle of their read units; V is stored
 //     row-major bf16 (fp8 codes are widened exactly on the way in) and read
 //     with ds_read_b64_tr_b16, whose 4x16 transpose yields the V^T operand.
 //   * Softmax in fp32, exp2 domain with log2(e) and (fp8) the q/k scales in
@@ -87,9 +88,19 @@ __device__ __forceinline__ int v_chunk(int r, int c) {
 
 
 
-__device__ __forceinline__ void lds_dma16(const void *gsrc, void *ldst) {
-  __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void *)gsrc,
-                                   (__attribute__((address_space(3))) void *)ldst, 16, 0, 0);
+// Buffer descriptor over [base, base + bytes): raw (stride 0), untyped
+// 32-bit data format as gfx9-family untyped buffer loads expect.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes,
+                                           0x00020000);
+}
+
+// 16 bytes per lane from rsrc + soff + voff straight into LDS at ldst + 16 * lane
+// (buffer_load_dwordx4 ... lds): no VGPR staging and no 64-bit address math.
+__device__ __forceinline__ void lds_dma16(__amdgpu_buffer_rsrc_t rs, uint32_t voff, uint32_t soff,
+                                          void *ldst) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (__attribute__((address_space(3))) void *)ldst, 16,
+                                           voff, soff, 0, 0);
 }
 
 template <int DT, int D, int BLK>
@@ -103,6 +114,7 @@ struct Attn {
   typedef typename std::conditional<DT == kFP8, i32x8, bf16x8>::type frag_t;
 
   const uint8_t *k, *v;
+  __amdgpu_buffer_rsrc_t krs, vrs;  // this kv head's K and V
   int seq, I, w, lane, half, l32, qi;
   size_t kvrow0;  // g * seq
   float scale2;
@@ -110,7 +122,8 @@ struct Attn {
   f32x16 oacc[DTL];
   float m_used, l;
   // per-lane byte offsets (loop constants)
-  int kdma[KPW / 64], vdma[DT == kBF16 ? VPW / 64 : 1], krow[KPW / 64], vrow[DT == kBF16 ? VPW / 64 : 1];
+  uint32_t kdma[KPW / 64], vdma[DT == kBF16 ? VPW / 64 : 1];
+  int krow[KPW / 64], vrow[DT == kBF16 ? VPW / 64 : 1];
   int koff[DK], voff[DTL];
   uint4 vreg[VPER];
 
@@ -147,27 +160,26 @@ struct Attn {
   // V) go straight to LDS; fp8 V comes back in registers for widening.
   __device__ __forceinline__ void issue(int J, int sub, uint8_t *Kb, uint16_t *Vb) {
     const int j0 = J * BLK + sub * KT;
-    const uint8_t *kb = k + (kvrow0 + j0) * RB;
-    const uint8_t *vb = v + (kvrow0 + j0) * (DT == kBF16 ? D * 2 : RB);
+    const uint32_t ksoff = (uint32_t)j0 * RB, vsoff = (uint32_t)j0 * (D * 2);
     if (j0 + KT <= seq) {
 #pragma unroll
-      for (int it = 0; it < KPW / 64; ++it) lds_dma16(kb + kdma[it], Kb + (w * KPW + it * 64) * 16);
+      for (int it = 0; it < KPW / 64; ++it) lds_dma16(krs, kdma[it], ksoff, Kb + (w * KPW + it * 64) * 16);
       if constexpr (DT == kBF16) {
 #pragma unroll
         for (int it = 0; it < VPW / 64; ++it)
-          lds_dma16(vb + vdma[it], (uint8_t *)Vb + (w * VPW + it * 64) * 16);
+          lds_dma16(vrs, vdma[it], vsoff, (uint8_t *)Vb + (w * VPW + it * 64) * 16);
       }
     } else {
       // ragged last block: rows past the end re-read the last row (finite data
       // whose keys are masked as causal-future for every valid query)
 #pragma unroll
       for (int it = 0; it < KPW / 64; ++it)
-        lds_dma16(kb + kdma[it] - max(0, j0 + krow[it] - (seq - 1)) * RB,
+        lds_dma16(krs, kdma[it] - (uint32_t)max(0, j0 + krow[it] - (seq - 1)) * RB, ksoff,
                   Kb + (w * KPW + it * 64) * 16);
       if constexpr (DT == kBF16) {
 #pragma unroll
         for (int it = 0; it < VPW / 64; ++it)
-          lds_dma16(vb + vdma[it] - max(0, j0 + vrow[it] - (seq - 1)) * (D * 2),
+          lds_dma16(vrs, vdma[it] - (uint32_t)max(0, j0 + vrow[it] - (seq - 1)) * (D * 2), vsoff,
                     (uint8_t *)Vb + (w * VPW + it * 64) * 16);
       }
     }
@@ -331,7 +343,7 @@ __global__ __launch_bounds__(BLK * 2, 256 / BLK) void attn_mfma_kernel(
   A T;
   const int tid = threadIdx.x;
   T.lane = tid & 63;
-  T.w = tid >> 6;
+  T.w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: scalar LDS bases
   T.half = T.lane >> 5;
   T.l32 = T.lane & 31;
   const int grp = hq / hkv;
@@ -356,6 +368,8 @@ __global__ __launch_bounds__(BLK * 2, 256 / BLK) void attn_mfma_kernel(
   T.k = k;
   T.v = v;
   T.kvrow0 = (size_t)g * seq;
+  T.krs = make_rsrc(k + T.kvrow0 * RB, (uint32_t)seq * RB);
+  T.vrs = make_rsrc(v + T.kvrow0 * (DT == kBF16 ? D * 2 : RB), (uint32_t)seq * (DT == kBF16 ? D * 2 : RB));
   T.qi = I * BLK + T.w * 32 + T.l32;
   const int half = T.half, qi = T.qi;
   const size_t row = (size_t)h * nb + I;
