@@ -30,9 +30,10 @@
 //     row-major bf16 (fp8 codes are widened exactly on the way in) and read
 //     with ds_read_b64_tr_b16, whose 4x16 transpose yields the V^T operand.
 //   * Softmax in fp32, exp2 domain with log2(e) and (fp8) the q/k scales in
-//     one factor; the max is taken on raw scores (max3), the exponent is one
-//     FMA, and the output is rescaled only when the running max grows by more
-//     than 2^8.
+//     one factor; the exponent is one FMA against a reference max that moves
+//     only when a lane's partial sum of probabilities passes 2^8 (then the
+//     tile's row max is taken, the output rescaled and P recomputed), so the
+//     common path has no max reduction at all.
 #include <type_traits>
 
 #include "device.h"
@@ -43,9 +44,10 @@ namespace bsp {
 typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
-// Rescale the accumulators only when the running max grows by more than this
-// (log2 units): probabilities then stay below 2^8, well inside bf16/fp32.
-constexpr float kRescaleSlack = 8.0f;
+// The accumulators are rescaled only when a lane's partial sum of
+// probabilities for a sub-tile exceeds this bound, so every probability stays
+// at or below 2^8, well inside bf16 and fp32.
+constexpr float kRescaleBound = 256.0f;
 
 template <int DT, int D, int BLK>
 struct AttnCfg {
@@ -271,16 +273,41 @@ struct Attn {
     bf16x8 va[2][DTL];
     load_v(va[0], Vb, 0);
     if (diag) mask_diag(s, j0);
-    // ---- running max on raw scores; rescale only on a large increase
-    float mx = -INFINITY;
+    // ---- P = exp2(s * scale2 - m) against the current reference max m,
+    //      packed to bf16 for the MFMA; the row sum accumulates the fp32
+    //      values (two partial sums break the add chain).
+    bf16x8 pb[NJ];
+    float l0, l1;
+    auto exps = [&](float mneg) {
+      l0 = 0.f;
+      l1 = 0.f;
 #pragma unroll
-    for (int kt = 0; kt < KTS; ++kt)
+      for (int j = 0; j < NJ; ++j) {
+        const int kt = j / 2, st = j % 2;
 #pragma unroll
-      for (int r = 0; r < 16; r += 2) mx = fmaxf(fmaxf(mx, s[kt][r]), s[kt][r + 1]);
-    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-    const float mx2 = mx * scale2;
-    if (__any(mx2 > m_used + kRescaleSlack)) {
-      const float mnew = fmaxf(m_used, mx2);
+        for (int s8 = 0; s8 < 8; s8 += 2) {
+          const float p0 = __builtin_amdgcn_exp2f(fmaf(s[kt][st * 8 + s8], scale2, mneg));
+          const float p1 = __builtin_amdgcn_exp2f(fmaf(s[kt][st * 8 + s8 + 1], scale2, mneg));
+          l0 += p0;
+          l1 += p1;
+          pb[j][s8] = (__bf16)p0;
+          pb[j][s8 + 1] = (__bf16)p1;
+        }
+      }
+    };
+    exps(m_used == -INFINITY ? 0.f : -m_used);
+    // ---- The reference max moves only when needed: when a lane's partial
+    //      sum exceeds kRescaleBound = 2^8 (which bounds every term of it), or
+    //      while a row has no reference yet.  Then the row max of the tile is
+    //      taken, the accumulators are rescaled and P is recomputed.
+    if (__any(!(l0 + l1 <= kRescaleBound) || m_used == -INFINITY)) {
+      float mx = -INFINITY;
+#pragma unroll
+      for (int kt = 0; kt < KTS; ++kt)
+#pragma unroll
+        for (int r = 0; r < 16; r += 2) mx = fmaxf(fmaxf(mx, s[kt][r]), s[kt][r + 1]);
+      mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+      const float mnew = fmaxf(m_used, mx * scale2);
       const float alpha = mnew == -INFINITY ? 1.f : __builtin_amdgcn_exp2f(m_used - mnew);
       l *= alpha;
 #pragma unroll
@@ -288,24 +315,7 @@ struct Attn {
 #pragma unroll
         for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
       m_used = mnew;
-    }
-    const float mneg = m_used == -INFINITY ? 0.f : -m_used;
-    // ---- P = exp2(s * scale2 - m) packed to bf16 for the MFMA; the row sum
-    //      accumulates the fp32 values (two partial sums break the add chain)
-    bf16x8 pb[NJ];
-    float l0 = 0.f, l1 = 0.f;
-#pragma unroll
-    for (int j = 0; j < NJ; ++j) {
-      const int kt = j / 2, st = j % 2;
-#pragma unroll
-      for (int s8 = 0; s8 < 8; s8 += 2) {
-        const float p0 = __builtin_amdgcn_exp2f(fmaf(s[kt][st * 8 + s8], scale2, mneg));
-        const float p1 = __builtin_amdgcn_exp2f(fmaf(s[kt][st * 8 + s8 + 1], scale2, mneg));
-        l0 += p0;
-        l1 += p1;
-        pb[j][s8] = (__bf16)p0;
-        pb[j][s8 + 1] = (__bf16)p1;
-      }
+      exps(m_used == -INFINITY ? 0.f : -m_used);
     }
     l += l0 + l1;
     // ---- O^T += V^T P^T.  Step j covers keys j*16 + [0,16); operand slot s of
