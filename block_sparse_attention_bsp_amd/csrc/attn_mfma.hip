@@ -14,26 +14,30 @@
 //     the 8 XCDs evenly, every XCD serves whole GQA groups: the 64 workgroups
 //     resident on an XCD walk the same K/V blocks in the same order, so K/V
 //     come from that XCD's L2.
-//   * Scores are computed transposed, S^T = K Q^T (v_mfma_f32_32x32x16_bf16,
-//     or v_mfma_scale_f32_32x32x64_f8f6f4 with unit scales for e4m3): each lane
-//     holds one query and 16 keys of a 32x32 tile, so the softmax reductions
-//     are in-lane plus one exchange with the lane 32 away.
-//   * The output is accumulated transposed, O^T += V^T P^T (bf16 MFMA): every
-//     accumulator of a lane belongs to its own query.  P^T is the B operand
-//     straight from the score registers; the key order inside a 16-key step is
-//     permuted identically on both operands.
+//   * Scores are computed transposed in 16x16 tiles, S^T = K Q^T
+//     (v_mfma_f32_16x16x32_bf16, or one v_mfma_scale_f32_16x16x128_f8f6f4
+//     with unit scales per tile for e4m3).  Lane 16g + r owns query r of each
+//     of the wave's two 16-query tiles and keys 4g .. 4g+3 of every 16-key
+//     tile, so everything on the common path stays in-lane; a query's four
+//     lanes meet only to rescale and at the end.
+//   * The output is accumulated transposed, O^T += V^T P^T (16x16x32 bf16):
+//     every accumulator of a lane belongs to one of its two queries.  P^T is
+//     the B operand straight from the score registers (slots 0-3 and 4-7 are
+//     the lane's rows of two consecutive key tiles); the V^T operand reads the
+//     same keys with two ds_read_b64_tr_b16, whose 4x16 transpose yields it.
 //   * K/V sub-tiles of 64 keys are double-buffered in LDS and filled one
 //     sub-tile ahead by buffer_load_dwordx4 ... lds (no VGPR staging; one
 //     buffer descriptor per kv head, the sub-tile position as the scalar
 //     offset, loop-invariant lane offsets), so the load of sub-tile i+1
-//     overlaps the MFMAs of sub-tile i; one barrier per sub-tile.  K rows carry an XOR swizzle of their read units; V is stored
-//     row-major bf16 (fp8 codes are widened exactly on the way in) and read
-//     with ds_read_b64_tr_b16, whose 4x16 transpose yields the V^T operand.
+//     overlaps the MFMAs of sub-tile i; one barrier per sub-tile.  K rows
+//     carry an XOR swizzle of their read units; V is stored row-major bf16
+//     (fp8 codes are widened exactly on the way in).
 //   * Softmax in fp32, exp2 domain with log2(e) and (fp8) the q/k scales in
-//     one factor; the exponent is one FMA against a reference max that moves
-//     only when a lane's partial sum of probabilities passes 2^8 (then the
-//     tile's row max is taken, the output rescaled and P recomputed), so the
-//     common path has no max reduction at all.
+//     one factor; the exponent is one FMA against a reference max per query
+//     that moves only when a lane's partial sum of probabilities passes 2^8
+//     (then the query's max over the sub-tile is taken, the output rescaled
+//     and P recomputed), so the common path has no max reduction at all.
+
 #include <type_traits>
 
 #include "device.h"
@@ -53,18 +57,21 @@ template <int DT, int D, int BLK>
 struct AttnCfg {
   static constexpr int ES = DT == kFP8 ? 1 : 2;  // bytes per Q/K element
   static constexpr int RB = D * ES;              // bytes per K row
-  static constexpr int KSTEP = DT == kFP8 ? 64 : 16;
-  static constexpr int LB = KSTEP / 2 * ES;      // bytes per lane per S^T step (16 or 32)
+  // S^T MFMA: 16x16x32 bf16 (16 bytes per lane per step), or one
+  // 16x16x128 f8f6f4 per tile for e4m3 (32 bytes per lane; d = 64 fills
+  // half of it and zeroes the rest).
+  static constexpr int LB = DT == kFP8 ? (D == 128 ? 32 : 16) : 16;  // bytes read per lane per step
   static constexpr int CPU = LB / 16;            // 16-byte chunks per read unit
-  static constexpr int DK = D / KSTEP;           // S^T k-steps
+  static constexpr int DK = DT == kFP8 ? 1 : D / 32;  // S^T k-steps
   static constexpr int UNITS = RB / LB;          // read units per K row
   static constexpr int KRPW = RB >= 256 ? 1 : 256 / RB;  // K rows per 256-byte window
-  static constexpr int NW = BLK / 32;
+  static constexpr int NW = BLK / 32;            // wavefronts: 32 queries each
   static constexpr int NT = NW * 64;
   static constexpr int KT = 64;                  // keys per LDS sub-tile
   static constexpr int NSUB = BLK / KT;
-  static constexpr int KTS = KT / 32;
-  static constexpr int DTL = D / 32;
+  static constexpr int NKT = KT / 16;            // 16-key S^T tiles per sub-tile
+  static constexpr int NJ = KT / 32;             // 32-key PV steps per sub-tile
+  static constexpr int NDT = D / 16;             // 16-wide d tiles of O^T
   static constexpr int KBYTES = KT * RB;         // K sub-tile bytes
   static constexpr int VBYTES = KT * D * 2;      // V sub-tile bytes (bf16)
   static constexpr int KCH = KBYTES / 16;        // 16-byte chunks per K sub-tile
@@ -109,7 +116,8 @@ template <int DT, int D, int BLK>
 struct Attn {
   using C = AttnCfg<DT, D, BLK>;
   static constexpr int RB = C::RB, LB = C::LB, DK = C::DK, KT = C::KT;
-  static constexpr int KTS = C::KTS, DTL = C::DTL, NSUB = C::NSUB, NW = C::NW, NT = C::NT;
+  static constexpr int NKT = C::NKT, NJ = C::NJ, NDT = C::NDT, NSUB = C::NSUB, NW = C::NW,
+                       NT = C::NT;
   static constexpr int KPW = C::KCH / NW;               // K DMA chunks per wave
   static constexpr int VPW = (C::VBYTES / 16) / NW;     // V DMA chunks per wave (bf16)
   static constexpr int VPER = C::VCHK / NT > 0 ? C::VCHK / NT : 1;  // fp8 V chunks per thread
@@ -117,16 +125,19 @@ struct Attn {
 
   const uint8_t *k, *v;
   __amdgpu_buffer_rsrc_t krs, vrs;  // this kv head's K and V
-  int seq, I, w, lane, half, l32, qi;
-  size_t kvrow0;  // g * seq
+  // lane = 16 * g + r: in every 16x16 tile the lane owns column r (a query)
+  // and rows 4g .. 4g + 3 (keys of S^T, dimensions of O^T)
+  int seq, I, w, lane, g, r16;
+  int qi[2];      // the lane's two queries (query tiles 0 and 1 of the wave)
+  size_t kvrow0;  // kv head * seq
   float scale2;
-  frag_t qf[DK];
-  f32x16 oacc[DTL];
-  float m_used, l;
+  frag_t qf[2][DK];
+  f32x4 oacc[NDT][2];
+  float m_used[2], l[2];
   // per-lane byte offsets (loop constants)
   uint32_t kdma[KPW / 64], vdma[DT == kBF16 ? VPW / 64 : 1];
   int krow[KPW / 64], vrow[DT == kBF16 ? VPW / 64 : 1];
-  int koff[DK], voff[DTL];
+  int koff[DK], voff[D / 32];
   uint4 vreg[VPER];
 
   __device__ __forceinline__ void setup() {
@@ -147,14 +158,18 @@ struct Attn {
         vrow[it] = r;
       }
     }
+    // K (A operand): key row r16 of a tile, read unit ks * 4 + g (bf16) or g (fp8)
 #pragma unroll
-    for (int kk = 0; kk < DK; ++kk) koff[kk] = l32 * RB + k_unit<DT, D, BLK>(l32, kk * 2 + half) * LB;
-    const int vg = lane >> 4, vi = lane & 15, vrr = vi >> 2, vss = vi & 3;
-    const int r0 = (vg >> 1) * 4 + vrr;
+    for (int ks = 0; ks < DK; ++ks)
+      koff[ks] = r16 * RB + k_unit<DT, D, BLK>(r16, (DT == kFP8 ? 0 : ks * 4) + g) * LB;
+    // V^T (A operand) via ds_read_b64_tr_b16: in lane group g, lane r16 supplies
+    // row 4g + r16 / 4 (a key) and columns 4 (r16 % 4) .. + 3 of a 16-wide d
+    // tile; odd d tiles sit 32 bytes after even ones (same 64-byte group).
+    const int vr = 4 * g + (r16 >> 2), vq = r16 & 3;
 #pragma unroll
-    for (int db = 0; db < DTL; ++db) {
-      const int dcol = db * 32 + (vg & 1) * 16 + vss * 4;
-      voff[db] = r0 * (D * 2) + v_chunk<D>(r0, dcol >> 3) * 16 + (dcol & 7) * 2;
+    for (int dp = 0; dp < D / 32; ++dp) {
+      const int dcol = dp * 32 + vq * 4;
+      voff[dp] = vr * (D * 2) + v_chunk<D>(vr, dcol >> 3) * 16 + (dcol & 7) * 2;
     }
   }
 
@@ -214,123 +229,138 @@ struct Attn {
     }
   }
 
-  __device__ __forceinline__ void mask_diag(f32x16 (&s)[KTS], int j0) {
-    // Element r of tile kt is key j0 + kt*32 + (r/4)*8 + half*4 + r%4.
+  __device__ __forceinline__ void mask_diag(f32x4 (&s)[NKT][2], int j0) {
+    // Element e of tile (kt, qt) is key j0 + kt*16 + 4g + e of query qi[qt].
 #pragma unroll
-    for (int kt = 0; kt < KTS; ++kt)
+    for (int kt = 0; kt < NKT; ++kt)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int key = j0 + kt * 32 + (r / 4) * 8 + half * 4 + (r % 4);
-        if (key > qi) s[kt][r] = -INFINITY;
+      for (int qt = 0; qt < 2; ++qt)
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          if (j0 + kt * 16 + 4 * g + e > qi[qt]) s[kt][qt][e] = -INFINITY;
+  }
+
+  __device__ __forceinline__ void load_k(frag_t (&a)[NKT], const uint8_t *__restrict__ Kb, int ks) {
+#pragma unroll
+    for (int kt = 0; kt < NKT; ++kt) {
+      if constexpr (DT == kFP8 && LB == 16) {
+        uint4 lo;
+        __builtin_memcpy(&lo, Kb + koff[ks] + kt * 16 * RB, 16);
+        const uint4 ab[2] = {lo, make_uint4(0, 0, 0, 0)};
+        __builtin_memcpy(&a[kt], ab, 32);
+      } else {
+        __builtin_memcpy(&a[kt], Kb + koff[ks] + kt * 16 * RB, sizeof(frag_t));
       }
-  }
-
-  __device__ __forceinline__ void load_k(frag_t (&a)[KTS], const uint8_t *__restrict__ Kb, int kk) {
-#pragma unroll
-    for (int kt = 0; kt < KTS; ++kt)
-      __builtin_memcpy(&a[kt], Kb + koff[kk] + kt * 32 * RB, sizeof(frag_t));
-  }
-
-  __device__ __forceinline__ void load_v(bf16x8 (&a)[DTL], const uint16_t *__restrict__ Vb, int j) {
-    // step j = (kt, st) covers keys j*16 + [0, 16)
-#pragma unroll
-    for (int db = 0; db < DTL; ++db) {
-      const uint8_t *p0 = (const uint8_t *)Vb + voff[db] + j * 16 * (D * 2);
-      const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4 *)p0);
-      const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4 *)(p0 + 8 * D * 2));
-      a[db] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
     }
+  }
+
+  // V^T fragment of d tile dt for PV step j: keys j*32 + 4g + [0,4) and
+  // j*32 + 16 + 4g + [0,4), matching the P^T slots of the lane.
+  __device__ __forceinline__ bf16x8 load_v(const uint16_t *__restrict__ Vb, int j, int dt) {
+    const uint8_t *p0 = (const uint8_t *)Vb + voff[dt / 2] + (dt % 2) * 32 + j * 32 * (D * 2);
+    const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4 *)p0);
+    const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4 *)(p0 + 16 * D * 2));
+    return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+  }
+
+  __device__ __forceinline__ f32x4 mma_qk(const frag_t &a, const frag_t &b, f32x4 c) {
+    if constexpr (DT == kFP8)
+      return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 0, 127, 0, 127);
+    else
+      return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
   }
 
   // One 64-key sub-tile from LDS.  LDS fragments are double-buffered in
   // registers one MFMA group ahead; scheduling barriers keep that order.
   __device__ __forceinline__ void compute(const uint8_t *__restrict__ Kb,
                                           const uint16_t *__restrict__ Vb, int j0, bool diag) {
-    constexpr int NJ = KTS * 2;  // 16-key PV steps per sub-tile
-    // ---- S^T = K Q^T; the KTS accumulators alternate between MFMAs
-    f32x16 s[KTS];
+    // ---- S^T = K Q^T: NKT key tiles x 2 query tiles, 16x16 each
+    f32x4 s[NKT][2];
 #pragma unroll
-    for (int kt = 0; kt < KTS; ++kt) s[kt] = f32x16{};
-    frag_t ka[2][KTS];
+    for (int kt = 0; kt < NKT; ++kt) s[kt][0] = s[kt][1] = f32x4{};
+    frag_t ka[2][NKT];
     __builtin_amdgcn_s_setprio(1);
     load_k(ka[0], Kb, 0);
 #pragma unroll
-    for (int kk = 0; kk < DK; ++kk) {
-      if (kk + 1 < DK) load_k(ka[(kk + 1) & 1], Kb, kk + 1);
+    for (int ks = 0; ks < DK; ++ks) {
+      if (ks + 1 < DK) load_k(ka[(ks + 1) & 1], Kb, ks + 1);
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-      for (int kt = 0; kt < KTS; ++kt) {
-        if constexpr (DT == kFP8)
-          s[kt] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(ka[kk & 1][kt], qf[kk], s[kt],
-                                                                  0, 0, 0, 127, 0, 127);
-        else
-          s[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[kk & 1][kt], qf[kk], s[kt], 0, 0, 0);
-      }
+      for (int kt = 0; kt < NKT; ++kt)
+#pragma unroll
+        for (int qt = 0; qt < 2; ++qt) s[kt][qt] = mma_qk(ka[ks & 1][kt], qf[qt][ks], s[kt][qt]);
       __builtin_amdgcn_sched_barrier(0);
     }
     __builtin_amdgcn_s_setprio(0);
     // V^T fragments of the first PV step load while the softmax runs
-    bf16x8 va[2][DTL];
-    load_v(va[0], Vb, 0);
+    bf16x8 va[2];
+    va[0] = load_v(Vb, 0, 0);
     if (diag) mask_diag(s, j0);
-    // ---- P = exp2(s * scale2 - m) against the current reference max m,
-    //      packed to bf16 for the MFMA; the row sum accumulates the fp32
-    //      values (two partial sums break the add chain).
-    bf16x8 pb[NJ];
-    float l0, l1;
-    auto exps = [&](float mneg) {
-      l0 = 0.f;
-      l1 = 0.f;
+    // ---- P = exp2(s * scale2 - m) against a reference max m per query,
+    //      packed to bf16 for the MFMA; the row sums take the fp32 values.
+    //      Slot e of P^T step j for query tile qt: key tile 2j + e/4, row e%4.
+    bf16x8 pb[NJ][2];
+    float ps[2];
+    auto exps = [&]() {
 #pragma unroll
-      for (int j = 0; j < NJ; ++j) {
-        const int kt = j / 2, st = j % 2;
+      for (int qt = 0; qt < 2; ++qt) {
+        const float mneg = m_used[qt] == -INFINITY ? 0.f : -m_used[qt];
+        float a0 = 0.f, a1 = 0.f;
 #pragma unroll
-        for (int s8 = 0; s8 < 8; s8 += 2) {
-          const float p0 = __builtin_amdgcn_exp2f(fmaf(s[kt][st * 8 + s8], scale2, mneg));
-          const float p1 = __builtin_amdgcn_exp2f(fmaf(s[kt][st * 8 + s8 + 1], scale2, mneg));
-          l0 += p0;
-          l1 += p1;
-          pb[j][s8] = (__bf16)p0;
-          pb[j][s8 + 1] = (__bf16)p1;
-        }
+        for (int kt = 0; kt < NKT; ++kt)
+#pragma unroll
+          for (int e = 0; e < 4; e += 2) {
+            const float p0 = __builtin_amdgcn_exp2f(fmaf(s[kt][qt][e], scale2, mneg));
+            const float p1 = __builtin_amdgcn_exp2f(fmaf(s[kt][qt][e + 1], scale2, mneg));
+            a0 += p0;
+            a1 += p1;
+            pb[kt / 2][qt][(kt % 2) * 4 + e] = (__bf16)p0;
+            pb[kt / 2][qt][(kt % 2) * 4 + e + 1] = (__bf16)p1;
+          }
+        ps[qt] = a0 + a1;
       }
     };
-    exps(m_used == -INFINITY ? 0.f : -m_used);
+    exps();
     // ---- The reference max moves only when needed: when a lane's partial
-    //      sum exceeds kRescaleBound = 2^8 (which bounds every term of it), or
-    //      while a row has no reference yet.  Then the row max of the tile is
-    //      taken, the accumulators are rescaled and P is recomputed.
-    if (__any(!(l0 + l1 <= kRescaleBound) || m_used == -INFINITY)) {
-      float mx = -INFINITY;
+    //      sum for a query exceeds kRescaleBound = 2^8 (which bounds every
+    //      term of it), or while a query has no reference yet.  Then the
+    //      query's max over the sub-tile is taken across the four lanes that
+    //      hold it, the output is rescaled and P recomputed.
+    if (__any(!(ps[0] <= kRescaleBound) || !(ps[1] <= kRescaleBound) ||
+              m_used[0] == -INFINITY || m_used[1] == -INFINITY)) {
 #pragma unroll
-      for (int kt = 0; kt < KTS; ++kt)
+      for (int qt = 0; qt < 2; ++qt) {
+        float mx = -INFINITY;
 #pragma unroll
-        for (int r = 0; r < 16; r += 2) mx = fmaxf(fmaxf(mx, s[kt][r]), s[kt][r + 1]);
-      mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-      const float mnew = fmaxf(m_used, mx * scale2);
-      const float alpha = mnew == -INFINITY ? 1.f : __builtin_amdgcn_exp2f(m_used - mnew);
-      l *= alpha;
+        for (int kt = 0; kt < NKT; ++kt)
+          mx = fmaxf(fmaxf(mx, fmaxf(s[kt][qt][0], s[kt][qt][1])), fmaxf(s[kt][qt][2], s[kt][qt][3]));
+        mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
+        mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+        const float mnew = fmaxf(m_used[qt], mx * scale2);
+        const float alpha = mnew == -INFINITY ? 1.f : __builtin_amdgcn_exp2f(m_used[qt] - mnew);
+        l[qt] *= alpha;
 #pragma unroll
-      for (int db = 0; db < DTL; ++db)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
-      m_used = mnew;
-      exps(m_used == -INFINITY ? 0.f : -m_used);
+        for (int dt = 0; dt < NDT; ++dt) oacc[dt][qt] *= alpha;
+        m_used[qt] = mnew;
+      }
+      exps();
     }
-    l += l0 + l1;
-    // ---- O^T += V^T P^T.  Step j covers keys j*16 + [0,16); operand slot s of
-    //      lane half `half` is key j*16 + (s/4)*8 + half*4 + s%4 on both
-    //      operands.  The DTL accumulators alternate between MFMAs.
+    l[0] += ps[0];
+    l[1] += ps[1];
+    // ---- O^T += V^T P^T: d tiles x 2 query tiles, 32 keys per step
     __builtin_amdgcn_s_setprio(1);
 #pragma unroll
-    for (int j = 0; j < NJ; ++j) {
-      if (j + 1 < NJ) load_v(va[(j + 1) & 1], Vb, j + 1);
-      __builtin_amdgcn_sched_barrier(0);
+    for (int j = 0; j < NJ; ++j)
 #pragma unroll
-      for (int db = 0; db < DTL; ++db)
-        oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[j & 1][db], pb[j], oacc[db], 0, 0, 0);
-      __builtin_amdgcn_sched_barrier(0);
-    }
+      for (int dt = 0; dt < NDT; ++dt) {
+        const int n = j * NDT + dt;
+        if (n + 1 < NJ * NDT) va[(n + 1) & 1] = load_v(Vb, (n + 1) / NDT, (n + 1) % NDT);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int qt = 0; qt < 2; ++qt)
+          oacc[dt][qt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va[n & 1], pb[j][qt], oacc[dt][qt], 0, 0, 0);
+        __builtin_amdgcn_sched_barrier(0);
+      }
     __builtin_amdgcn_s_setprio(0);
   }
 };
@@ -344,7 +374,7 @@ __global__ __launch_bounds__(BLK * 2, 256 / BLK) void attn_mfma_kernel(
     int seq, int nb, float sm_scale_log2, int xcd_map) {
   using A = Attn<DT, D, BLK>;
   using C = typename A::C;
-  constexpr int RB = C::RB, LB = C::LB, DK = C::DK, KT = C::KT, DTL = C::DTL, NSUB = C::NSUB;
+  constexpr int RB = C::RB, LB = C::LB, DK = C::DK, KT = C::KT, NSUB = C::NSUB;
   __shared__ __attribute__((aligned(16))) uint8_t Ks0[C::KBYTES];
   __shared__ __attribute__((aligned(16))) uint8_t Ks1[C::KBYTES];
   __shared__ __attribute__((aligned(16))) uint16_t Vs0[KT * D];
@@ -354,8 +384,8 @@ __global__ __launch_bounds__(BLK * 2, 256 / BLK) void attn_mfma_kernel(
   const int tid = threadIdx.x;
   T.lane = tid & 63;
   T.w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: scalar LDS bases
-  T.half = T.lane >> 5;
-  T.l32 = T.lane & 31;
+  T.g = T.lane >> 4;
+  T.r16 = T.lane & 15;
   const int grp = hq / hkv;
   int I, h;
   {
@@ -380,31 +410,37 @@ __global__ __launch_bounds__(BLK * 2, 256 / BLK) void attn_mfma_kernel(
   T.kvrow0 = (size_t)g * seq;
   T.krs = make_rsrc(k + T.kvrow0 * RB, (uint32_t)seq * RB);
   T.vrs = make_rsrc(v + T.kvrow0 * (DT == kBF16 ? D * 2 : RB), (uint32_t)seq * (DT == kBF16 ? D * 2 : RB));
-  T.qi = I * BLK + T.w * 32 + T.l32;
-  const int half = T.half, qi = T.qi;
+  T.qi[0] = I * BLK + T.w * 32 + T.r16;
+  T.qi[1] = T.qi[0] + 16;
   const size_t row = (size_t)h * nb + I;
   T.scale2 = sm_scale_log2;
   if constexpr (DT == kFP8) T.scale2 *= q_scale[h] * k_scale[g];
   T.setup();
 
-  // Q fragments: B operand of S^T = K Q^T, query qi, LB bytes per step.
+  // Q fragments: B operand of S^T = K Q^T.  Lane (g, r16) holds query
+  // qi[qt], dimensions ks*32 + 8g .. + 8 (bf16) or LB bytes at g*LB (fp8).
 #pragma unroll
-  for (int kk = 0; kk < DK; ++kk) {
-    const uint8_t *src = q + ((size_t)h * seq + min(qi, seq - 1)) * RB + kk * 2 * LB + half * LB;
-    uint4 a = *(const uint4 *)src, b = a;
-    if constexpr (LB == 32) b = *(const uint4 *)(src + 16);
-    if (qi >= seq) a = b = make_uint4(0, 0, 0, 0);
-    if constexpr (LB == 32) {
-      const uint4 ab[2] = {a, b};
-      __builtin_memcpy(&T.qf[kk], ab, 32);
-    } else {
-      __builtin_memcpy(&T.qf[kk], &a, 16);
+  for (int qt = 0; qt < 2; ++qt) {
+    const int qq = T.qi[qt];
+#pragma unroll
+    for (int ks = 0; ks < DK; ++ks) {
+      const uint8_t *src = q + ((size_t)h * seq + min(qq, seq - 1)) * RB +
+                           (DT == kFP8 ? T.g * LB : (ks * 32 + 8 * T.g) * 2);
+      uint4 a = *(const uint4 *)src, b = make_uint4(0, 0, 0, 0);
+      if constexpr (LB == 32) b = *(const uint4 *)(src + 16);
+      if (qq >= seq) a = b = make_uint4(0, 0, 0, 0);
+      if constexpr (DT == kFP8) {
+        const uint4 ab[2] = {a, b};
+        __builtin_memcpy(&T.qf[qt][ks], ab, 32);
+      } else {
+        __builtin_memcpy(&T.qf[qt][ks], &a, 16);
+      }
     }
   }
 #pragma unroll
-  for (int db = 0; db < DTL; ++db) T.oacc[db] = f32x16{};
-  T.m_used = -INFINITY;
-  T.l = 0.f;
+  for (int dt = 0; dt < C::NDT; ++dt) T.oacc[dt][0] = T.oacc[dt][1] = f32x4{};
+  T.m_used[0] = T.m_used[1] = -INFINITY;
+  T.l[0] = T.l[1] = 0.f;
 
   const int nblk = kv_idx ? max(0, min(kv_cnt[row], nb)) : I + 1;
   const int32_t *ilist = kv_idx ? kv_idx + row * nb : nullptr;
@@ -457,25 +493,29 @@ __global__ __launch_bounds__(BLK * 2, 256 / BLK) void attn_mfma_kernel(
     }
   }
 
-  const float lt = T.l + __shfl_xor(T.l, 32, 64);
-  if (qi < seq) {
-    float inv = lt > 0.f ? 1.f / lt : 0.f;
-    if constexpr (DT == kFP8) inv *= v_scale[g];
-    uint16_t *orow = o + ((size_t)h * seq + qi) * D;
+  // each query's row sum is split over the four lanes 16 apart
 #pragma unroll
-    for (int db = 0; db < DTL; ++db)
+  for (int qt = 0; qt < 2; ++qt) {
+    float lt = T.l[qt];
+    lt += __shfl_xor(lt, 16, 64);
+    lt += __shfl_xor(lt, 32, 64);
+    const int qq = T.qi[qt];
+    if (qq < seq) {
+      float inv = lt > 0.f ? 1.f / lt : 0.f;
+      if constexpr (DT == kFP8) inv *= v_scale[g];
+      uint16_t *orow = o + ((size_t)h * seq + qq) * D;
 #pragma unroll
-      for (int gq = 0; gq < 4; ++gq) {
-        const int d0 = db * 32 + gq * 8 + half * 4;
+      for (int dt = 0; dt < C::NDT; ++dt) {
         uint2 pk;
-        pk.x = f32_to_bf16_bits(T.oacc[db][gq * 4 + 0] * inv) |
-               (f32_to_bf16_bits(T.oacc[db][gq * 4 + 1] * inv) << 16);
-        pk.y = f32_to_bf16_bits(T.oacc[db][gq * 4 + 2] * inv) |
-               (f32_to_bf16_bits(T.oacc[db][gq * 4 + 3] * inv) << 16);
-        *(uint2 *)(orow + d0) = pk;
+        pk.x = f32_to_bf16_bits(T.oacc[dt][qt][0] * inv) |
+               (f32_to_bf16_bits(T.oacc[dt][qt][1] * inv) << 16);
+        pk.y = f32_to_bf16_bits(T.oacc[dt][qt][2] * inv) |
+               (f32_to_bf16_bits(T.oacc[dt][qt][3] * inv) << 16);
+        *(uint2 *)(orow + dt * 16 + 4 * T.g) = pk;
       }
-    if (lse && half == 0)
-      lse[(size_t)h * seq + qi] = lt > 0.f ? (T.m_used + log2f(lt)) * kLn2 : -INFINITY;
+      if (lse && T.g == 0)
+        lse[(size_t)h * seq + qq] = lt > 0.f ? (T.m_used[qt] + log2f(lt)) * kLn2 : -INFINITY;
+    }
   }
 }
 
