@@ -292,9 +292,12 @@ struct Attn {
       __builtin_amdgcn_sched_barrier(0);
     }
     __builtin_amdgcn_s_setprio(0);
-    // V^T fragments of the first PV step load while the softmax runs
-    bf16x8 va[2];
-    va[0] = load_v(Vb, 0, 0);
+    // V^T fragments: a ring of four, three PV MFMA pairs ahead; the first
+    // three load while the softmax runs
+    constexpr int NV = NJ * NDT;
+    bf16x8 va[4];
+#pragma unroll
+    for (int n = 0; n < 3 && n < NV; ++n) va[n] = load_v(Vb, n / NDT, n % NDT);
     if (diag) mask_diag(s, j0);
     // ---- P = exp2(s * scale2 - m) against a reference max m per query,
     //      packed to bf16 for the MFMA; the row sums take the fp32 values.
@@ -305,15 +308,15 @@ struct Attn {
 #pragma unroll
       for (int qt = 0; qt < 2; ++qt) {
         const float mneg = m_used[qt] == -INFINITY ? 0.f : -m_used[qt];
-        float a0 = 0.f, a1 = 0.f;
+        float a0, a1;
 #pragma unroll
         for (int kt = 0; kt < NKT; ++kt)
 #pragma unroll
           for (int e = 0; e < 4; e += 2) {
             const float p0 = __builtin_amdgcn_exp2f(fmaf(s[kt][qt][e], scale2, mneg));
             const float p1 = __builtin_amdgcn_exp2f(fmaf(s[kt][qt][e + 1], scale2, mneg));
-            a0 += p0;
-            a1 += p1;
+            a0 = (kt == 0 && e == 0) ? p0 : a0 + p0;
+            a1 = (kt == 0 && e == 0) ? p1 : a1 + p1;
             pb[kt / 2][qt][(kt % 2) * 4 + e] = (__bf16)p0;
             pb[kt / 2][qt][(kt % 2) * 4 + e + 1] = (__bf16)p1;
           }
@@ -354,11 +357,11 @@ struct Attn {
 #pragma unroll
       for (int dt = 0; dt < NDT; ++dt) {
         const int n = j * NDT + dt;
-        if (n + 1 < NJ * NDT) va[(n + 1) & 1] = load_v(Vb, (n + 1) / NDT, (n + 1) % NDT);
+        if (n + 3 < NV) va[(n + 3) & 3] = load_v(Vb, (n + 3) / NDT, (n + 3) % NDT);
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int qt = 0; qt < 2; ++qt)
-          oacc[dt][qt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va[n & 1], pb[j][qt], oacc[dt][qt], 0, 0, 0);
+          oacc[dt][qt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va[n & 3], pb[j][qt], oacc[dt][qt], 0, 0, 0);
         __builtin_amdgcn_sched_barrier(0);
       }
     __builtin_amdgcn_s_setprio(0);
