@@ -279,7 +279,6 @@ struct Attn {
 #pragma unroll
     for (int kt = 0; kt < NKT; ++kt) s[kt][0] = s[kt][1] = f32x4{};
     frag_t ka[2][NKT];
-    __builtin_amdgcn_s_setprio(1);
     load_k(ka[0], Kb, 0);
 #pragma unroll
     for (int ks = 0; ks < DK; ++ks) {
@@ -291,7 +290,9 @@ struct Attn {
         for (int qt = 0; qt < 2; ++qt) s[kt][qt] = mma_qk(ka[ks & 1][kt], qf[qt][ks], s[kt][qt]);
       __builtin_amdgcn_sched_barrier(0);
     }
-    __builtin_amdgcn_s_setprio(0);
+    // From here to the end of the sub-tile (softmax and PV) the wave runs at
+    // raised priority: a SIMD's other wave fills the gaps with its S^T MFMAs.
+    __builtin_amdgcn_s_setprio(1);
     // V^T fragments: a ring of four, three PV MFMA pairs ahead; the first
     // three load while the softmax runs
     constexpr int NV = NJ * NDT;
@@ -351,7 +352,6 @@ struct Attn {
     l[0] += ps[0];
     l[1] += ps[1];
     // ---- O^T += V^T P^T: d tiles x 2 query tiles, 32 keys per step
-    __builtin_amdgcn_s_setprio(1);
 #pragma unroll
     for (int j = 0; j < NJ; ++j)
 #pragma unroll
