@@ -210,8 +210,12 @@ def main():
     peak = PEAK_FP8_TFLOPS if c.dtype == "fp8" else PEAK_BF16_TFLOPS
     achieved = F_kept / (st_attn * 1e-3) / 1e12
     es = {"f32": 4, "bf16": 2, "fp8": 1}[c.dtype]
-    sbytes = scoring_bytes(hq, hkv, seq, d, B, es, kept_entries)
-    score_gbs = sbytes / ((st_score + st_mask) * 1e-3) / 1e9
+    scoring = None
+    if um is None:  # with a caller mask the scorer does not run
+        sbytes = scoring_bytes(hq, hkv, seq, d, B, es, kept_entries)
+        score_gbs = sbytes / ((st_score + st_mask) * 1e-3) / 1e9
+        scoring = {"bytes": sbytes, "GB/s": round(score_gbs, 1),
+                   "hbm_frac": round(score_gbs / PEAK_HBM_GBS, 4)}
 
     if a.copy_calibration:
         src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
@@ -247,8 +251,7 @@ def main():
         "density": round(density, 6),
         "kept_tflops": round(achieved, 3),
         "mfma_peak_frac": round(achieved / peak, 4),
-        "scoring": {"bytes": sbytes, "GB/s": round(score_gbs, 1),
-                    "hbm_frac": round(score_gbs / PEAK_HBM_GBS, 4)},
+        "scoring": scoring,
         "roofline": {"bound": "mfma", "achieved": round(achieved, 3), "peak": peak,
                      "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
                      "traffic": traffic, "kernel": "attn_mfma_kernel",
