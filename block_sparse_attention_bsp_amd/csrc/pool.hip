@@ -4,10 +4,12 @@
 //
 // HBM-bound: every byte of Q and K is read once, with non-temporal 16-byte
 // loads (nothing is reused within this pass, and streaming past the caches
-// raises the achieved read rate by about 15%).  One workgroup owns one
-// (head, block) pair, a contiguous B x d slab (32 KiB for bf16 at
+// raises the achieved read rate by about 15%).  One wavefront owns one
+// (head, block) slab, a contiguous B x d region (32 KiB for bf16 at
 // B = d = 128): lane t reads 16-byte column chunk t % CH of rows t / CH,
-// t / CH + RG, ...  Partial column sums meet in LDS.
+// t / CH + 64 / CH, ..., with all of a lane's loads for the slab in flight
+// together.  The lanes that share a column chunk then combine their partial
+// sums with cross-lane adds: no LDS and no barrier.
 #include "device.h"
 #include "internal.h"
 
@@ -22,78 +24,81 @@ __global__ __launch_bounds__(256) void pool_kernel(const uint8_t *__restrict__ q
                                                    const float *__restrict__ k_scale,
                                                    float *__restrict__ q_pool,
                                                    float *__restrict__ k_pool, int hq, int seq,
-                                                   int nb) {
+                                                   int nb, int nslab) {
   constexpr int ES = Storage<DT>::bytes;
   constexpr int VEC = 16 / ES;     // elements per 16-byte chunk
-  constexpr int CH = D / VEC;      // chunks per row
-  constexpr int RG = 256 / CH;     // row groups
-  constexpr int ITER = BLK / RG;   // rows per thread for a full block
-  static_assert(CH * RG == 256 && ITER * RG == BLK, "tiling");
-  __shared__ float part[RG][D + 1];
-
-  const int I = blockIdx.x;
-  const int hh = blockIdx.y;
+  constexpr int CH = D / VEC;      // chunks per row (4..32)
+  constexpr int RPL = 64 / CH;     // rows covered by one wave-wide load
+  constexpr int NLD = BLK / RPL;   // loads per lane for a whole slab
+  static_assert(CH * RPL == 64 && NLD * RPL == BLK, "tiling");
+  const int lane = threadIdx.x & 63;
+  const int sl = blockIdx.x * 4 + (threadIdx.x >> 6);  // one slab per wavefront
+  if (sl >= nslab) return;
+  const int hh = sl / nb, I = sl - hh * nb;
   const bool isq = hh < hq;
   const int h = isq ? hh : hh - hq;
   const int t0 = I * BLK;
   const int rows = min(BLK, seq - t0);
   const uint8_t *base = (isq ? q : k) + ((size_t)h * seq + t0) * D * ES;
-  const int c = threadIdx.x % CH;
-  const int r0 = threadIdx.x / CH;
+  const int c = lane % CH, r0 = lane / CH;
 
   float acc[VEC];
 #pragma unroll
   for (int e = 0; e < VEC; ++e) acc[e] = 0.f;
-
-  uint4 w[ITER];
+  constexpr int BATCH = NLD < 16 ? NLD : 16;
 #pragma unroll
-  for (int it = 0; it < ITER; ++it) {
-    const int r = r0 + it * RG;
-    const u32x4v *src = (const u32x4v *)(base + ((size_t)r * D + c * VEC) * ES);
-    const u32x4v t = r < rows ? __builtin_nontemporal_load(src) : u32x4v{0u, 0u, 0u, 0u};
-    w[it] = make_uint4(t.x, t.y, t.z, t.w);
-  }
+  for (int b0 = 0; b0 < NLD; b0 += BATCH) {
+    u32x4v w[BATCH];
 #pragma unroll
-  for (int it = 0; it < ITER; ++it) {
-    const uint32_t wd[4] = {w[it].x, w[it].y, w[it].z, w[it].w};
+    for (int it = 0; it < BATCH; ++it) {
+      const int r = r0 + (b0 + it) * RPL;
+      const u32x4v *src = (const u32x4v *)(base + ((size_t)r * D + c * VEC) * ES);
+      w[it] = r < rows ? __builtin_nontemporal_load(src) : u32x4v{0u, 0u, 0u, 0u};
+    }
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      if constexpr (DT == kF32) {
-        acc[j] += __uint_as_float(wd[j]);
-      } else if constexpr (DT == kBF16) {
-        acc[2 * j] += bf16_bits_to_f32(wd[j] & 0xFFFFu);
-        acc[2 * j + 1] += bf16_bits_to_f32(wd[j] >> 16);
-      } else {
-        const f32x2 lo = e4m3x2_to_f32(wd[j], false), hi = e4m3x2_to_f32(wd[j], true);
-        acc[4 * j] += lo.x;
-        acc[4 * j + 1] += lo.y;
-        acc[4 * j + 2] += hi.x;
-        acc[4 * j + 3] += hi.y;
+    for (int it = 0; it < BATCH; ++it) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const uint32_t wd = w[it][j];
+        if constexpr (DT == kF32) {
+          acc[j] += __uint_as_float(wd);
+        } else if constexpr (DT == kBF16) {
+          acc[2 * j] += bf16_bits_to_f32(wd & 0xFFFFu);
+          acc[2 * j + 1] += bf16_bits_to_f32(wd >> 16);
+        } else {
+          const f32x2 lo = e4m3x2_to_f32(wd, false), hi = e4m3x2_to_f32(wd, true);
+          acc[4 * j] += lo.x;
+          acc[4 * j + 1] += lo.y;
+          acc[4 * j + 2] += hi.x;
+          acc[4 * j + 3] += hi.y;
+        }
       }
     }
   }
+  // lanes c, c + CH, ... hold partial sums of the same columns
 #pragma unroll
-  for (int e = 0; e < VEC; ++e) part[r0][c * VEC + e] = acc[e];
-  __syncthreads();
-
-  float scale = 1.f;
-  if constexpr (DT == kFP8) scale = isq ? q_scale[h] : k_scale[h];
-  float *out = (isq ? q_pool : k_pool) + ((size_t)h * nb + I) * D;
-  const float inv = scale / (float)rows;
-  for (int e = threadIdx.x; e < D; e += 256) {
-    float s = 0.f;
+  for (int o = CH; o < 64; o <<= 1)
 #pragma unroll
-    for (int g = 0; g < RG; ++g) s += part[g][e];
-    out[e] = s * inv;
+    for (int e = 0; e < VEC; ++e) acc[e] += __shfl_xor(acc[e], o, 64);
+  if (lane < CH) {
+    float scale = 1.f;
+    if constexpr (DT == kFP8) scale = isq ? q_scale[h] : k_scale[h];
+    const float inv = scale / (float)rows;
+    float *out = (isq ? q_pool : k_pool) + ((size_t)h * nb + I) * D + c * VEC;
+#pragma unroll
+    for (int e = 0; e < VEC; e += 4)
+      *(float4 *)(out + e) =
+          make_float4(acc[e] * inv, acc[e + 1] * inv, acc[e + 2] * inv, acc[e + 3] * inv);
   }
 }
 
 template <int DT, int D, int BLK>
 static hipError_t launch_pool_t(const Shape &s, const void *q, const void *k, const float *qs,
                                 const float *ks, float *qp, float *kp, hipStream_t st) {
-  dim3 grid(s.nb, s.hq + s.hkv);
-  hipLaunchKernelGGL((pool_kernel<DT, D, BLK>), grid, dim3(256), 0, st, (const uint8_t *)q,
-                     (const uint8_t *)k, qs, ks, qp, kp, s.hq, s.seq, s.nb);
+  const int nslab = (s.hq + s.hkv) * s.nb;
+  hipLaunchKernelGGL((pool_kernel<DT, D, BLK>), dim3((nslab + 3) / 4), dim3(256), 0, st,
+                     (const uint8_t *)q, (const uint8_t *)k, qs, ks, qp, kp, s.hq, s.seq, s.nb,
+                     nslab);
   return hipGetLastError();
 }
 
