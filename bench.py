@@ -73,13 +73,18 @@ def kept_flops(cnt: np.ndarray, d: int, block: int, seq: int) -> float:
 
 
 def scoring_bytes(hq, hkv, seq, d, block, es, kept_entries):
+    """Minimal HBM bytes of pool + score + mask: read Q and K; write the
+    fp32 block means and read them back; write P (every entry, zeros above
+    the diagonal); read P's causal half (nothing else decides the mask);
+    write the mask, the kept indices and the counts."""
     nb = -(-seq // block)
-    rd = (hq + hkv) * seq * d * es                   # read Q, K
-    wr_pool = (hq + hkv) * nb * d * 4                 # write pooled rows
-    p = hq * nb * nb * 4                              # write P, read P
+    rd = (hq + hkv) * seq * d * es                    # read Q, K
+    pooled = 2 * (hq + hkv) * nb * d * 4              # write, then read, the means
+    p_wr = hq * nb * nb * 4                           # write P
+    p_rd = hq * nb * (nb + 1) // 2 * 4                # read P where J <= I
     mask = hq * nb * nb                               # write mask
     idx = kept_entries * 4 + hq * nb * 4              # write idx (kept) and counts
-    return rd + wr_pool + 2 * p + mask + idx
+    return rd + pooled + p_wr + p_rd + mask + idx
 
 
 def traffic_from_note():
