@@ -107,12 +107,106 @@ __global__ __launch_bounds__(256) void mask_kernel(const float *__restrict__ P,
   if (lane == 0) kv_cnt[row] = n;
 }
 
+// Rows of at most 256 * NS blocks under the max-based threshold: the row of
+// P is read from HBM once, all of a lane's loads in flight together, and kept
+// in registers for the decision and the compaction.
+template <int NS>
+__global__ __launch_bounds__(256) void mask_kernel_reg(const float *__restrict__ P,
+                                                       uint8_t *__restrict__ mask,
+                                                       int32_t *__restrict__ kv_idx,
+                                                       int32_t *__restrict__ kv_cnt, int rows,
+                                                       int nb, float gamma, int sink, int local) {
+  const int lane = threadIdx.x & 63;
+  const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (row >= rows) return;
+  const int I = row % nb;
+  const size_t off = (size_t)row * nb;
+  const bool vec = (nb & 3) == 0;  // rows are 16-byte aligned
+
+  float x[NS][4];
+  float m = -INFINITY;
+#pragma unroll
+  for (int t = 0; t < NS; ++t) {
+    const int J = t * 256 + 4 * lane;
+    if (J <= I) {
+      if (vec && J + 3 < nb) {
+        const float4 v = *(const float4 *)(P + off + J);
+        x[t][0] = v.x; x[t][1] = v.y; x[t][2] = v.z; x[t][3] = v.w;
+      } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) x[t][e] = J + e < nb ? P[off + J + e] : 0.f;
+      }
+    } else {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) x[t][e] = 0.f;
+    }
+  }
+#pragma unroll
+  for (int t = 0; t < NS; ++t)
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      if (t * 256 + 4 * lane + e <= I) m = fmaxf(m, x[t][e]);
+  const float thr = gamma * wave_max(m);
+
+  const uint64_t below = (1ull << lane) - 1ull;
+  int n = 0;
+#pragma unroll
+  for (int t = 0; t < NS; ++t) {
+    const int J = t * 256 + 4 * lane;
+    if (t * 256 >= nb) break;
+    bool keep[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int Je = J + e;
+      keep[e] = Je <= I && (x[t][e] >= thr || Je < sink || I - Je < local);
+    }
+    if (vec && J + 3 < nb) {
+      *(uint32_t *)(mask + off + J) = (uint32_t)keep[0] | ((uint32_t)keep[1] << 8) |
+                                      ((uint32_t)keep[2] << 16) | ((uint32_t)keep[3] << 24);
+    } else {
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        if (J + e < nb) mask[off + J + e] = keep[e] ? 1 : 0;
+    }
+    uint64_t bal[4];
+    int before = 0, total = 0;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      bal[e] = __ballot(keep[e]);
+      before += __popcll(bal[e] & below);
+      total += __popcll(bal[e]);
+    }
+    int mine = 0;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      if (keep[e]) kv_idx[off + n + before + mine] = J + e;
+      mine += keep[e] ? 1 : 0;
+    }
+    n += total;
+  }
+  if (lane == 0) kv_cnt[row] = n;
+}
+
 hipError_t launch_mask(const Shape &s, float gamma, int sink, int local, const float *score,
                        const uint8_t *user, uint8_t *mask, int32_t *idx, int32_t *cnt,
                        hipStream_t st) {
   const int rows = s.hq * s.nb;
-  hipLaunchKernelGGL(mask_kernel, dim3((rows + 3) / 4), dim3(256), 0, st, score, user, mask, idx,
-                     cnt, rows, s.nb, gamma, sink, local);
+  const dim3 grid((rows + 3) / 4), block(256);
+  if (!user && s.nb <= 256)
+    hipLaunchKernelGGL(mask_kernel_reg<1>, grid, block, 0, st, score, mask, idx, cnt, rows, s.nb,
+                       gamma, sink, local);
+  else if (!user && s.nb <= 512)
+    hipLaunchKernelGGL(mask_kernel_reg<2>, grid, block, 0, st, score, mask, idx, cnt, rows, s.nb,
+                       gamma, sink, local);
+  else if (!user && s.nb <= 1024)
+    hipLaunchKernelGGL(mask_kernel_reg<4>, grid, block, 0, st, score, mask, idx, cnt, rows, s.nb,
+                       gamma, sink, local);
+  else if (!user && s.nb <= 2048)
+    hipLaunchKernelGGL(mask_kernel_reg<8>, grid, block, 0, st, score, mask, idx, cnt, rows, s.nb,
+                       gamma, sink, local);
+  else
+    hipLaunchKernelGGL(mask_kernel, grid, block, 0, st, score, user, mask, idx, cnt, rows, s.nb,
+                       gamma, sink, local);
   return hipGetLastError();
 }
 
