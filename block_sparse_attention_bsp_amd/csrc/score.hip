@@ -4,21 +4,25 @@
 // Appendix B: query tiles against causally valid pooled key blocks, then a
 // global normalisation).
 //
-// One kernel, two passes over the causal block grid of a group of 32 query
-// blocks:
+// Two passes over the causal block grid of a group of 32 query blocks:
 //   pass 1  S^T tiles = Kbar Qbar^T (32 key blocks x 32 query blocks) on
 //           v_mfma_f32_32x32x2_f32 - fp32 products and sums, so the
 //           threshold downstream sees full-precision scores - reduced to the
-//           running row max and sum of exp and written out raw, transposed
-//           through LDS so that every store covers whole 128-byte row runs;
-//   pass 2  after a barrier the workgroup sweeps its 32 rows of P row-major
-//           with 16-byte accesses: P = exp(S - max) / sum from the raw
-//           scores on the causal part, zeros above it.
-// Each lane owns one query block (a column of S^T), so the row
-// reductions are in-lane plus one exchange with the lane 32 away; the four
-// wavefronts of a workgroup split the key-block tiles of the same 32 query
-// blocks and merge their row statistics through LDS.  The grid launches the
-// heaviest row groups of every head first.
+//           running row max and sum of exp;
+//   pass 2  after the row statistics meet, P = exp(S - max) / sum on the
+//           causal part, zeros above it.
+// Each lane owns one query block (a column of S^T), so the row reductions are
+// in-lane plus one exchange with the lane 32 away; the wavefronts of a
+// workgroup split the key-block tiles of the same 32 query blocks and merge
+// their row statistics through LDS.  The grid launches the heaviest row
+// groups of every head first.
+//
+// score_kernel_reg (rows of at most 1024 blocks): eight wavefronts with at
+// most four tiles each keep their raw scores in registers, so P is written
+// once, normalised, through an LDS transpose that makes every store cover
+// whole 128-byte row runs.  score_kernel (longer rows): four wavefronts write
+// the raw scores transposed the same way, then the workgroup sweeps its rows
+// row-major with 16-byte accesses and normalises them in place.
 #include "device.h"
 #include "internal.h"
 
@@ -218,13 +222,196 @@ __global__ __launch_bounds__(256) void score_kernel(const float *__restrict__ q_
   }
 }
 
+// Rows of at most 1024 key blocks: eight wavefronts split the key-block tiles
+// of the group (at most four each) and keep their raw scores in registers,
+// so P is written once, already normalised, and never read back.
+template <int D>
+__global__ __launch_bounds__(512) void score_kernel_reg(const float *__restrict__ q_pool,
+                                                        const float *__restrict__ k_pool,
+                                                        float *__restrict__ P, int hq, int hkv,
+                                                        int nb, float c2) {
+  constexpr int KS = D / 2;   // k-steps; step ks, lane half h <-> dimension ks + KS*h
+  constexpr int NWV = 8;      // wavefronts
+  constexpr int MAXT = 4;     // tiles per wavefront
+  __shared__ float red_m[NWV][32], red_l[NWV][32], row_m[32], row_inv[32];
+  __shared__ __attribute__((aligned(16))) float kt_s[NWV * 32 * (D + 4)];
+  const int G = (nb + 31) / 32;
+  const int grp = G - 1 - (int)blockIdx.y;
+  const int h = blockIdx.x;
+  const int g = h / (hq / hkv);
+  const int w = threadIdx.x >> 6, lane = threadIdx.x & 63, half = lane >> 5, l32 = lane & 31;
+  const int I0 = grp * 32;
+  const int rows = min(32, nb - I0);
+  const int Il = I0 + l32;  // this lane's query block
+  const bool row_ok = l32 < rows;
+  const int ntc = (I0 + rows - 1) / 32 + 1;  // key-block tiles touching the causal part
+  const bool vec = (nb & 3) == 0;             // rows of P are 16-byte aligned
+  float *pgrp = P + ((size_t)h * nb + I0) * nb;
+
+  float qb[KS];
+  {
+    const float *src = q_pool + ((size_t)h * nb + min(Il, nb - 1)) * D + KS * half;
+#pragma unroll
+    for (int i = 0; i < KS; i += 4) {
+      const float4 t = *(const float4 *)(src + i);
+      qb[i] = row_ok ? t.x : 0.f;
+      qb[i + 1] = row_ok ? t.y : 0.f;
+      qb[i + 2] = row_ok ? t.z : 0.f;
+      qb[i + 3] = row_ok ? t.w : 0.f;
+    }
+  }
+
+  constexpr int TF4 = 32 * D / 4 / 64;  // float4 per lane per tile
+  constexpr int RS = D + 4;             // padded LDS row stride (floats)
+  constexpr int TS = 33;                // transpose row stride (floats)
+  float *kt_lds = kt_s + w * 32 * RS;
+  // the tile goes global -> registers -> LDS in two halves (no prefetch:
+  // the SIMD's other wavefront covers the load latency)
+  auto load_stage = [&](int jt) {
+    const float *src = k_pool + ((size_t)g * nb + jt * 32) * D;
+    const int n = min(32, nb - jt * 32);
+#pragma unroll
+    for (int hb = 0; hb < 2; ++hb) {
+      float4 st[TF4 / 2];
+#pragma unroll
+      for (int i = 0; i < TF4 / 2; ++i) {
+        const int f = lane + 64 * (hb * (TF4 / 2) + i);
+        st[i] = f / (D / 4) < n ? *(const float4 *)(src + 4 * f) : make_float4(0.f, 0.f, 0.f, 0.f);
+      }
+#pragma unroll
+      for (int i = 0; i < TF4 / 2; ++i) {
+        const int f = lane + 64 * (hb * (TF4 / 2) + i);
+        *(float4 *)(kt_lds + (f / (D / 4)) * RS + (f % (D / 4)) * 4) = st[i];
+      }
+    }
+  };
+  auto mma = [&]() -> f32x16 {
+    const float *arow = kt_lds + l32 * RS + KS * half;
+    f32x16 acc = f32x16{};
+#pragma unroll
+    for (int i = 0; i < KS / 4; ++i) {
+      const float4 a = *(const float4 *)(arow + 4 * i);
+      acc = __builtin_amdgcn_mfma_f32_32x32x2f32(a.x, qb[4 * i], acc, 0, 0, 0);
+      acc = __builtin_amdgcn_mfma_f32_32x32x2f32(a.y, qb[4 * i + 1], acc, 0, 0, 0);
+      acc = __builtin_amdgcn_mfma_f32_32x32x2f32(a.z, qb[4 * i + 2], acc, 0, 0, 0);
+      acc = __builtin_amdgcn_mfma_f32_32x32x2f32(a.w, qb[4 * i + 3], acc, 0, 0, 0);
+    }
+    return acc;
+  };
+
+  // ---- pass 1: raw log2-domain scores held in registers, row max and sum
+  float held[MAXT][16];
+  float m = -INFINITY, l = 0.f;
+#pragma unroll
+  for (int t = 0; t < MAXT; ++t) {
+    const int jt = w + t * NWV;
+    if (jt < ntc) {
+      load_stage(jt);
+      const f32x16 acc = mma();
+      float tmax = -INFINITY;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int J = jt * 32 + (r / 4) * 8 + half * 4 + (r % 4);
+        held[t][r] = (J <= Il && J < nb) ? acc[r] * c2 : -INFINITY;
+        tmax = fmaxf(tmax, held[t][r]);
+      }
+      const float mn = fmaxf(m, tmax);
+      if (mn != -INFINITY) {
+        float acc_l = 0.f;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc_l += exp2f(held[t][r] - mn);
+        l = l * exp2f(m - mn) + acc_l;
+        m = mn;
+      }
+    }
+  }
+  {
+    const float mo = __shfl_xor(m, 32, 64), lo = __shfl_xor(l, 32, 64);
+    const float mn = fmaxf(m, mo);
+    if (mn != -INFINITY) {
+      l = (m == -INFINITY ? 0.f : l * exp2f(m - mn)) + (mo == -INFINITY ? 0.f : lo * exp2f(mo - mn));
+      m = mn;
+    }
+  }
+  if (half == 0) {
+    red_m[w][l32] = m;
+    red_l[w][l32] = l;
+  }
+  __syncthreads();
+  if (w == 0 && half == 0) {
+    float M = -INFINITY;
+#pragma unroll
+    for (int i = 0; i < NWV; ++i) M = fmaxf(M, red_m[i][l32]);
+    float L = 0.f;
+#pragma unroll
+    for (int i = 0; i < NWV; ++i)
+      if (red_m[i][l32] != -INFINITY) L += red_l[i][l32] * exp2f(red_m[i][l32] - M);
+    row_m[l32] = M;
+    row_inv[l32] = L > 0.f ? 1.f / L : 0.f;
+  }
+  __syncthreads();
+
+  // ---- pass 2: normalise the held tiles and write them through the wave's
+  // LDS slice, so that 8 lanes cover one row's 32 keys of a tile
+  {
+    const float M = row_m[l32], inv = row_inv[l32];
+    const int c4 = (lane & 7) * 4;
+#pragma unroll
+    for (int t = 0; t < MAXT; ++t) {
+      const int jt = w + t * NWV;
+      if (jt < ntc) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          kt_lds[l32 * TS + (r / 4) * 8 + half * 4 + (r % 4)] = exp2f(held[t][r] - M) * inv;
+#pragma unroll
+        for (int it = 0; it < 4; ++it) {
+          const int rr = it * 8 + (lane >> 3);
+          const float *tp = kt_lds + rr * TS + c4;
+          const int J = jt * 32 + c4;
+          float *dst = pgrp + (size_t)rr * nb + J;
+          if (rr < rows) {
+            if (vec && J + 3 < nb) {
+              *(float4 *)dst = make_float4(tp[0], tp[1], tp[2], tp[3]);
+            } else {
+#pragma unroll
+              for (int e = 0; e < 4; ++e)
+                if (J + e < nb) dst[e] = tp[e];
+            }
+          }
+        }
+      }
+    }
+  }
+  // zeros above the causal tiles, all threads, row-major
+  const int jend = ntc * 32;
+  if (jend < nb) {
+    if (vec) {
+      const int n4 = (nb - jend) / 4;
+      for (int e = threadIdx.x; e < rows * n4; e += 512) {
+        const int rr = e / n4, J = jend + (e - rr * n4) * 4;
+        *(float4 *)(pgrp + (size_t)rr * nb + J) = make_float4(0.f, 0.f, 0.f, 0.f);
+      }
+    } else {
+      const int n1 = nb - jend;
+      for (int e = threadIdx.x; e < rows * n1; e += 512) {
+        const int rr = e / n1;
+        pgrp[(size_t)rr * nb + jend + (e - rr * n1)] = 0.f;
+      }
+    }
+  }
+}
+
 template <int D>
 static hipError_t launch_score_t(const Shape &s, float c, const float *qp, const float *kp,
                                  float *S, hipStream_t st) {
   // heaviest row groups of every head first
   dim3 grid(s.hq, (s.nb + 31) / 32);
-  hipLaunchKernelGGL(score_kernel<D>, grid, dim3(256), 0, st, qp, kp, S, s.hq, s.hkv, s.nb,
-                     c * kLog2e);
+  if (s.nb <= 1024)
+    hipLaunchKernelGGL(score_kernel_reg<D>, grid, dim3(512), 0, st, qp, kp, S, s.hq, s.hkv, s.nb,
+                       c * kLog2e);
+  else
+    hipLaunchKernelGGL(score_kernel<D>, grid, dim3(256), 0, st, qp, kp, S, s.hq, s.hkv, s.nb,
+                       c * kLog2e);
   return hipGetLastError();
 }
 
