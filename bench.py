@@ -54,6 +54,8 @@ def parse():
                    help="planted strengths scaled by d**0.25 (logit units): the threshold prunes")
     p.add_argument("--user-density", type=float, default=None,
                    help="replace the scorer by a random caller mask of this density")
+    p.add_argument("--calibrate", type=float, default=None, metavar="TARGET",
+                   help="also time bsp_calibrate_gamma for this target density")
     p.add_argument("--copy-calibration", action="store_true",
                    help="also run one 1 GiB device copy (HBM counter calibration)")
     return p.parse_args()
@@ -228,6 +230,15 @@ def main():
         dst.copy_(src)
         torch.cuda.synchronize()
 
+    calib = None
+    if a.calibrate is not None and um is None:
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        g, dens, _, _, _ = bsp.calibrate_gamma(sc, seq, B, a.calibrate)
+        torch.cuda.synchronize()
+        calib = {"target": a.calibrate, "gamma": round(g, 6), "density": round(dens, 6),
+                 "ms": round((time.perf_counter() - t0) * 1e3, 3)}
+
     cpu = None
     if not a.no_cpu:
         cpu = cpu_baseline(c, mk.cpu().numpy(), a.cpu_rows)
@@ -263,6 +274,8 @@ def main():
                      "flops_per_launch": F_kept},
         "cpu_baseline": cpu,
     }
+    if calib is not None:
+        out["calibration"] = calib
     print(json.dumps(out), flush=True)
 
 

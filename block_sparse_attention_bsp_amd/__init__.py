@@ -20,7 +20,8 @@ import torch
 
 __all__ = [
     "BspError", "BspDesc", "lib", "library_path", "desc", "score", "mask", "attn_fwd", "prefill",
-    "bsp_score", "bsp_mask", "bsp_attn_fwd", "bsp_status_string", "bsp_abi_version",
+    "calibrate_gamma", "bsp_score", "bsp_mask", "bsp_attn_fwd", "bsp_calibrate_gamma",
+    "bsp_status_string", "bsp_abi_version",
     "DTYPE_F32", "DTYPE_BF16", "DTYPE_FP8_E4M3",
 ]
 
@@ -65,7 +66,10 @@ def lib():
         L.bsp_score.argtypes = [P, vp, vp, vp, vp, vp, vp]
         L.bsp_mask.argtypes = [P, vp, vp, vp, vp, vp, vp]
         L.bsp_attn_fwd.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp]
-        for f in (L.bsp_score, L.bsp_mask, L.bsp_attn_fwd):
+        f32 = ctypes.c_float
+        L.bsp_calibrate_gamma.argtypes = [P, vp, f32, f32, vp, vp, vp, vp,
+                                          ctypes.POINTER(f32), ctypes.POINTER(f32), vp]
+        for f in (L.bsp_score, L.bsp_mask, L.bsp_attn_fwd, L.bsp_calibrate_gamma):
             f.restype = ctypes.c_int32
         L.bsp_status_string.argtypes = [ctypes.c_int32]
         L.bsp_status_string.restype = ctypes.c_char_p
@@ -98,6 +102,13 @@ def bsp_mask(d: BspDesc, score_in, user_mask, mask_out, kv_idx, kv_cnt, stream) 
 
 def bsp_attn_fwd(d: BspDesc, q, k, v, kv_idx, kv_cnt, o, lse, stream) -> int:
     return lib().bsp_attn_fwd(ctypes.byref(d), q, k, v, kv_idx, kv_cnt, o, lse, stream)
+
+
+def bsp_calibrate_gamma(d: BspDesc, score_in, target: float, tol: float, mask_out, kv_idx,
+                        kv_cnt, cnt_host, gamma_out, density_out, stream) -> int:
+    return lib().bsp_calibrate_gamma(ctypes.byref(d), score_in, target, tol, mask_out, kv_idx,
+                                     kv_cnt, cnt_host, ctypes.byref(gamma_out),
+                                     ctypes.byref(density_out), stream)
 
 
 # ---------------------------------------------------------------- torch level
@@ -192,6 +203,28 @@ def mask(score_t: Optional[torch.Tensor], gamma: float, seq: int, block: int,
     cnt = torch.empty((hq, nb), dtype=torch.int32, device=ref.device)
     _check(bsp_mask(dsc, _ptr(score_t), _ptr(user_mask), _ptr(m), _ptr(idx), _ptr(cnt), _stream()))
     return m, idx, cnt
+
+
+def calibrate_gamma(score_t: torch.Tensor, seq: int, block: int, target: float,
+                    tol: float = 1e-4, sink_blocks: int = 1, local_blocks: int = 1):
+    """Threshold factor for a target density (bsp_calibrate_gamma; blocks the
+    host).  Returns (gamma, density, mask, kv_idx, kv_cnt) at that gamma."""
+    hq, nb, _ = score_t.shape
+    if nb != -(-seq // block):
+        raise BspError(2, "score does not match seq and block")
+    _shape(score_t, (hq, nb, nb), "score")
+    if score_t.dtype != torch.float32:
+        raise BspError(3, "score must be float32")
+    dsc = desc(hq, 1, seq, 64, block, DTYPE_F32, sink_blocks=sink_blocks,
+               local_blocks=local_blocks)
+    m = torch.empty((hq, nb, nb), dtype=torch.uint8, device=score_t.device)
+    idx = torch.empty((hq, nb, nb), dtype=torch.int32, device=score_t.device)
+    cnt = torch.empty((hq, nb), dtype=torch.int32, device=score_t.device)
+    host = torch.empty((hq * nb,), dtype=torch.int32)
+    g, dens = ctypes.c_float(), ctypes.c_float()
+    _check(bsp_calibrate_gamma(dsc, _ptr(score_t), target, tol, _ptr(m), _ptr(idx), _ptr(cnt),
+                               ctypes.c_void_p(host.data_ptr()), g, dens, _stream()))
+    return g.value, dens.value, m, idx, cnt
 
 
 def attn_fwd(q, k, v, block: int, kv_idx=None, kv_cnt=None, sm_scale: float = 0.0,

@@ -112,6 +112,59 @@ bsp_status bsp_attn_fwd(const bsp_desc *desc, const void *q, const void *k, cons
   return hip_status(e);
 }
 
+bsp_status bsp_calibrate_gamma(const bsp_desc *desc, const float *score, float target, float tol,
+                               uint8_t *mask, int32_t *kv_idx, int32_t *kv_cnt, int32_t *cnt_host,
+                               float *gamma_out, float *density_out, void *stream) {
+  bsp_status st = check_desc(desc, false);
+  if (st != BSP_OK) return st;
+  if (!(target > 0.f && target <= 1.f) || !(tol > 0.f && tol < 1.f)) return BSP_ERR_BAD_VALUE;
+  if (desc->sink_blocks < 0 || desc->local_blocks < 0) return BSP_ERR_BAD_VALUE;
+  if (!gamma_out || !density_out) return BSP_ERR_NULL_POINTER;
+  if (desc->seq == 0) {
+    *gamma_out = 1.f;
+    *density_out = 1.f;
+    return BSP_OK;
+  }
+  if (!score || !kv_idx || !kv_cnt || !cnt_host) return BSP_ERR_NULL_POINTER;
+  const Shape s = shape_of(desc);
+  hipStream_t hs = (hipStream_t)stream;
+  const size_t rows = (size_t)s.hq * s.nb;
+  const double causal = (double)s.hq * s.nb * (s.nb + 1) / 2.0;
+  auto density = [&](float g, double *dens) -> bsp_status {
+    if (bsp::launch_mask(s, g, desc->sink_blocks, desc->local_blocks, score, nullptr, mask, kv_idx,
+                         kv_cnt, hs) != hipSuccess)
+      return BSP_ERR_HIP;
+    if (hipMemcpyAsync(cnt_host, kv_cnt, rows * sizeof(int32_t), hipMemcpyDeviceToHost, hs) !=
+            hipSuccess ||
+        hipStreamSynchronize(hs) != hipSuccess)
+      return BSP_ERR_HIP;
+    double kept = 0.0;
+    for (size_t i = 0; i < rows; ++i) kept += cnt_host[i];
+    *dens = kept / causal;
+    return BSP_OK;
+  };
+  double d = 0.0;
+  if ((st = density(1.f, &d)) != BSP_OK) return st;
+  if (d >= target) {
+    *gamma_out = 1.f;
+    *density_out = (float)d;
+    return BSP_OK;
+  }
+  float lo = 0.f, hi = 1.f;  // density(lo) >= target > density(hi)
+  while (hi - lo > tol) {
+    const float mid = 0.5f * (lo + hi);
+    if ((st = density(mid, &d)) != BSP_OK) return st;
+    if (d >= target)
+      lo = mid;
+    else
+      hi = mid;
+  }
+  if ((st = density(lo, &d)) != BSP_OK) return st;  // leave the buffers at lo
+  *gamma_out = lo;
+  *density_out = (float)d;
+  return BSP_OK;
+}
+
 const char *bsp_status_string(int32_t status) {
   switch (status) {
     case BSP_OK: return "BSP_OK";

@@ -44,7 +44,7 @@
 extern "C" {
 #endif
 
-#define BSP_ABI_VERSION 1
+#define BSP_ABI_VERSION 2
 
 typedef enum bsp_status {
   BSP_OK = 0,
@@ -154,6 +154,33 @@ bsp_status bsp_mask(const bsp_desc *desc, const float *score, const uint8_t *use
 bsp_status bsp_attn_fwd(const bsp_desc *desc, const void *q, const void *k, const void *v,
                         const int32_t *kv_idx, const int32_t *kv_cnt, void *o, float *lse,
                         void *stream);
+
+/*
+ * bsp_calibrate_gamma - host helper that picks the threshold factor for a
+ * target share of kept blocks (Appendix A "Hyperparameter Configurations":
+ * the single threshold hyperparameter is calibrated on computational density,
+ * about 70% at 4K, with block size and structural retention held fixed).
+ *
+ * density(gamma) = sum of kv_cnt / (hq * nb * (nb + 1) / 2) for the masks
+ * bsp_mask builds from `score` with desc's sink_blocks and local_blocks.  It
+ * never increases with gamma (the kept sets nest), so bisection on [0, 1]
+ * (midpoints in float) finds the largest gamma, to within tol, whose density
+ * is at least target; if gamma = 1 already keeps target, the result is 1.
+ *
+ * score:     device float [hq][nb][nb] from bsp_score
+ * target:    0 < target <= 1
+ * tol:       0 < tol < 1; bisection stops when the bracket is this narrow
+ * mask, kv_idx, kv_cnt: device work buffers as for bsp_mask (mask may be
+ *            NULL); on return they hold bsp_mask's result at *gamma_out
+ * cnt_host:  host int32 [hq * nb], staging for the counts
+ * gamma_out, density_out: host; the chosen gamma and its density
+ * Blocks the calling thread: every step launches the mask kernel on stream,
+ * copies the counts to cnt_host and waits for the stream.  desc->gamma is not
+ * read.  Allocates nothing.  seq == 0 gives gamma 1 and density 1.
+ */
+bsp_status bsp_calibrate_gamma(const bsp_desc *desc, const float *score, float target, float tol,
+                               uint8_t *mask, int32_t *kv_idx, int32_t *kv_cnt, int32_t *cnt_host,
+                               float *gamma_out, float *density_out, void *stream);
 
 /* Static description of a status code (host, never NULL). */
 const char *bsp_status_string(int32_t status);

@@ -115,6 +115,34 @@ def mask(P: Optional[np.ndarray], gamma: float, sink_blocks: int = 1, local_bloc
     return m, idx, cnt
 
 
+def calibrate_gamma(P: np.ndarray, target: float, tol: float = 1e-4, sink_blocks: int = 1,
+                    local_blocks: int = 1):
+    """The threshold factor that keeps a target share of the causal blocks
+    (FlashPrefill summary page, Appendix A "Hyperparameter Configurations":
+    the threshold is calibrated on computational density).  density(gamma) is
+    the kept share of causal blocks under ``mask``; it never increases with
+    gamma, so bisection on [0, 1] with float32 midpoints returns the largest
+    gamma (to within tol) whose density is at least target, or 1 when gamma = 1
+    already keeps it.  Returns (gamma, density)."""
+    hq, nb, _ = P.shape
+    causal = hq * nb * (nb + 1) / 2.0
+
+    def density(g):
+        return mask(P, float(g), sink_blocks, local_blocks)[2].sum() / causal
+
+    d = density(np.float32(1.0))
+    if d >= target:
+        return 1.0, float(d)
+    lo, hi = np.float32(0.0), np.float32(1.0)
+    while hi - lo > np.float32(tol):
+        mid = np.float32(0.5) * (lo + hi)
+        if density(mid) >= target:
+            lo = mid
+        else:
+            hi = mid
+    return float(lo), float(density(lo))
+
+
 def attn(q, k, v, dtype: str, block: int, block_mask: np.ndarray, sm_scale: Optional[float] = None,
          q_scale=None, k_scale=None, v_scale=None, rows: Optional[np.ndarray] = None):
     """Exact attention per query token over its kept, causally visible keys.

@@ -27,8 +27,8 @@ def built():
 
 
 def test_header_declares_the_entry_points():
-    assert _declared() == ["bsp_abi_version", "bsp_attn_fwd", "bsp_mask", "bsp_score",
-                           "bsp_status_string"]
+    assert _declared() == ["bsp_abi_version", "bsp_attn_fwd", "bsp_calibrate_gamma", "bsp_mask",
+                           "bsp_score", "bsp_status_string"]
 
 
 def test_library_exports_every_declared_symbol():
@@ -123,3 +123,21 @@ def test_python_layer_raises_bsp_error():
     x = torch.zeros(2, 64, 64)
     with pytest.raises(bsp.BspError):
         bsp.score(x, x, 64)  # host tensors are rejected before the C call
+
+
+def test_calibrate_gamma_host_checks():
+    import ctypes as C
+    d = bsp.desc(4, 1, 1024, 64, 64, bsp.DTYPE_F32)
+    fake = C.c_void_p(0x1000)  # never dereferenced: every case fails before a launch
+    g, dens = C.c_float(), C.c_float()
+    for target, tol in [(0.0, 1e-4), (1.5, 1e-4), (float("nan"), 1e-4), (0.5, 0.0), (0.5, 1.0)]:
+        assert bsp.bsp_calibrate_gamma(d, fake, target, tol, fake, fake, fake, fake, g, dens,
+                                       None) == 4
+    assert bsp.lib().bsp_calibrate_gamma(C.byref(d), fake, 0.5, 1e-4, fake, fake, fake, fake,
+                                         None, C.byref(dens), None) == 1
+    assert bsp.bsp_calibrate_gamma(d, None, 0.5, 1e-4, fake, fake, fake, fake, g, dens,
+                                   None) == 1
+    d0 = bsp.desc(4, 1, 0, 64, 64, bsp.DTYPE_F32)
+    assert bsp.bsp_calibrate_gamma(d0, None, 0.5, 1e-4, None, None, None, None, g, dens,
+                                   None) == 0
+    assert g.value == 1.0 and dens.value == 1.0

@@ -197,6 +197,61 @@ def test_mask_nesting_in_gamma_and_forced_blocks():
                 assert idx[h, I, :cnt[h, I]].tolist() == np.flatnonzero(m[h, I]).tolist()
 
 
+def _exact_calibration(P, target, sink, local):
+    """Exhaustive answer: density only changes at the ratios P / row max, so
+    the largest gamma with density >= target is the largest such ratio (or 1)
+    whose kept share reaches the target.  Evaluated by counting, not through
+    the oracle's mask."""
+    hq, nb, _ = P.shape
+    I = np.arange(nb)[:, None]
+    J = np.arange(nb)[None, :]
+    causal = J <= I
+    forced = causal & ((J < sink) | (I - J < local))
+    pmax = np.where(causal, P, -np.inf).max(-1, keepdims=True)
+    ratios = np.where(causal, P / pmax, np.nan)
+    total = hq * nb * (nb + 1) / 2
+
+    def dens(g):
+        return ((causal & (P >= g * pmax)) | forced).sum() / total
+
+    if dens(1.0) >= target:
+        return 1.0
+    best = 0.0
+    for r in np.unique(ratios[~np.isnan(ratios)]):
+        if r <= 1.0 and dens(r) >= target:
+            best = max(best, r)
+    return best
+
+
+@pytest.mark.parametrize("seed,target", [(0, 0.3), (1, 0.5), (2, 0.7), (3, 0.9), (0, 0.05)])
+def test_calibrate_gamma_brackets_the_exact_answer(seed, target):
+    c = gen.make_s1(seed)
+    _, P, _ = _pipeline(c, 0.1)
+    tol = 1e-4
+    g, d = oracle.calibrate_gamma(P, target, tol)
+    exact = _exact_calibration(P, target, 1, 1)
+    assert d >= target
+    if exact == 1.0:
+        assert g == 1.0
+    else:
+        assert exact - tol <= g <= exact
+        # just above the exact answer the density falls below the target
+        _, _, cnt = oracle.mask(P, min(1.0, exact + 1e-7), 1, 1)
+        assert cnt.sum() / (c.hq * c.nb * (c.nb + 1) / 2) < target
+
+
+def test_calibrate_gamma_edges_and_monotone_in_target():
+    c = gen.make_s1(1)
+    _, P, _ = _pipeline(c, 0.1)
+    assert oracle.calibrate_gamma(P, 1.0)[1] == 1.0
+    # forced blocks alone reach a tiny target: gamma 1
+    assert oracle.calibrate_gamma(P, 1e-3) == (1.0, oracle.calibrate_gamma(P, 1e-3)[1])
+    gs = [oracle.calibrate_gamma(P, t)[0] for t in (0.2, 0.4, 0.6, 0.8, 0.95)]
+    assert all(a >= b for a, b in zip(gs, gs[1:]))
+    # wider structural retention never needs a smaller gamma for the same target
+    assert oracle.calibrate_gamma(P, 0.6, sink_blocks=3, local_blocks=3)[0] >= gs[2]
+
+
 def test_user_mask_is_anded_with_causal_without_forced_blocks():
     rng = np.random.default_rng(0)
     um = (rng.random((3, 8, 8)) < 0.4).astype(np.uint8)

@@ -128,6 +128,28 @@ def test_long_kv_lists(dtype):
     print(f"  max-abs O err {err:.2e}", flush=True)
 
 
+@pytest.mark.parametrize("which,target", [("s1_0", 0.3), ("s1_1", 0.7), ("llama_4k", 0.7)])
+def test_calibrate_gamma_matches_oracle(which, target):
+    """Bisection on the GPU masks lands on the oracle's gamma; the buffers
+    it leaves behind are the mask at that gamma."""
+    announce(f"calibrate gamma {which} target {target}")
+    c = gen.make_s1(int(which[-1])) if which.startswith("s1") else gen.make_config(1)
+    d = H.dev(c)
+    _, _, sc = bsp.score(d["q"], d["k"], c.block, q_scale=d["q_scale"], k_scale=d["k_scale"])
+    tol = 1e-4
+    g, dens, m, idx, cnt = bsp.calibrate_gamma(sc, c.seq, c.block, target, tol)
+    torch.cuda.synchronize()
+    orc = oracle.prefill(c, with_attn=False)
+    og, odens = oracle.calibrate_gamma(orc["P"], float(np.float32(target)), tol)
+    print(f"  gpu gamma {g:.6f} density {dens:.4f}; oracle gamma {og:.6f} density {odens:.4f}",
+          flush=True)
+    assert dens >= np.float32(target)
+    assert abs(g - og) <= tol and abs(dens - odens) <= 2.0 / (c.hq * c.nb * (c.nb + 1) / 2)
+    m2, idx2, cnt2 = bsp.mask(sc, g, c.seq, c.block)
+    torch.cuda.synchronize()
+    assert torch.equal(m, m2) and torch.equal(cnt, cnt2)
+
+
 def test_gamma0_equals_dense_path_bitwise():
     announce("gamma=0 vs dense")
     c = gen.make_case(4, 2, 1024, 128, 128, "bf16", 5, rope=True, n_vert=4)
