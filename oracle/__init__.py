@@ -47,6 +47,8 @@ def lib():
         L.oracle_pool.argtypes = [i32, i32, i32, i32, i32, vp, vp, vp]
         L.oracle_score.argtypes = [i32, i32, i32, i32, vp, vp, dbl, vp, vp]
         L.oracle_mask.argtypes = [i32, i32, vp, vp, dbl, i32, i32, vp, vp, vp]
+        L.oracle_score_arith.argtypes = [i32, i32, i32, i32, i32, i32, vp, vp, vp, dbl,
+                                         ctypes.c_long, vp, vp]
         L.oracle_attn.argtypes = [i32, i32, i32, i32, i32, i32, vp, vp, vp, vp, vp, vp, dbl,
                                   vp, i64, vp, vp, vp]
         L.oracle_decode_e4m3fn.argtypes = [ctypes.c_uint8]
@@ -99,6 +101,25 @@ def score(qbar: np.ndarray, kbar: np.ndarray, c: float):
     P = np.empty((hq, nb, nb), np.float64)
     lib().oracle_score(hq, hkv, nb, d, _p(qbar), _p(kbar), float(c), _p(S), _p(P))
     return S, P
+
+
+def score_arith(q: np.ndarray, k: np.ndarray, dtype: str, block: int, c: float, hkv: int,
+                q_scale=None, k_scale=None, rows: Optional[np.ndarray] = None) -> np.ndarray:
+    """Per-query block approximation (see oracle_score_arith): P[h, I, J] is
+    the mean over the tokens of block I of their softmax over the pooled key
+    blocks J <= I.  rows: optional flat ids h*nb + I; then the result is
+    [len(rows), nb], else [hq, nb, nb]."""
+    q = np.ascontiguousarray(q)
+    hq, seq, d = q.shape
+    nb = -(-seq // block)
+    kbar = pool(k, dtype, block, k_scale)
+    assert kbar.shape[0] == hkv
+    r = _c(rows, np.int64)
+    n = hq * nb if r is None else r.shape[0]
+    out = np.empty((n, nb), np.float64)
+    lib().oracle_score_arith(hq, hkv, seq, d, block, _DT[dtype], _p(q),
+                             _p(_c(q_scale, np.float32)), _p(kbar), float(c), n, _p(r), _p(out))
+    return out.reshape(hq, nb, nb) if r is None else out
 
 
 def mask(P: Optional[np.ndarray], gamma: float, sink_blocks: int = 1, local_blocks: int = 1,

@@ -158,6 +158,59 @@ int oracle_score(int hq, int hkv, int nb, int d, const double *qbar, const doubl
   return 0;
 }
 
+/* Per-query block approximation (section 3 "Instantaneous Pattern Discovery":
+ * pooled key blocks stand in for their tokens, and the block-level
+ * significance is the average over the queries of a block; "Block
+ * Approximation for Kernel Optimization": the result lives on the
+ * (L/B) x (L/B) grid).  For every query token i of block I and every
+ * causally valid key block J <= I:
+ *   s_iJ = c * q_i . kbar_J,   p_iJ = exp(s_iJ) / sum_{J' <= I} exp(s_iJ')
+ *   P[I][J] = mean over the valid tokens i of block I of p_iJ,  0 for J > I.
+ * q: [hq][seq][d] storage values (fp8 codes times q_scale[h]); kbar: pooled
+ * keys [hkv][nb][d] from oracle_pool.  rows: NULL for every (h, I), output
+ * [hq][nb][nb]; else nrow flat row ids h*nb + I, output [nrow][nb]. */
+int oracle_score_arith(int hq, int hkv, int seq, int d, int block, int dtype, const void *q,
+                       const float *q_scale, const double *kbar, double c, long nrow,
+                       const long *rows, double *P) {
+  init_tables();
+  int nb = (seq + block - 1) / block, grp = hq / hkv;
+  long n = rows ? nrow : (long)hq * nb;
+#pragma omp parallel
+  {
+    double *s = (double *)malloc(sizeof(double) * (size_t)nb);
+    double *qi = (double *)malloc(sizeof(double) * (size_t)d);
+#pragma omp for schedule(dynamic, 4)
+    for (long t = 0; t < n; ++t) {
+      long r = rows ? rows[t] : t;
+      int h = (int)(r / nb), I = (int)(r % nb), g = h / grp;
+      double *prow = P + (size_t)t * nb;
+      double qs = q_scale ? (double)q_scale[h] : 1.0;
+      for (int J = 0; J < nb; ++J) prow[J] = 0.0;
+      int i0 = I * block, i1 = i0 + block < seq ? i0 + block : seq;
+      for (int i = i0; i < i1; ++i) {
+        for (int e = 0; e < d; ++e) qi[e] = load(q, dtype, ((size_t)h * seq + i) * d + e) * qs;
+        double m = -INFINITY, z = 0.0;
+        for (int J = 0; J <= I; ++J) {
+          const double *kj = kbar + ((size_t)g * nb + J) * d;
+          double acc = 0.0;
+          for (int e = 0; e < d; ++e) acc += qi[e] * kj[e];
+          s[J] = c * acc;
+          if (s[J] > m) m = s[J];
+        }
+        for (int J = 0; J <= I; ++J) z += exp(s[J] - m);
+        for (int J = 0; J <= I; ++J) prow[J] += exp(s[J] - m) / z;
+      }
+      for (int J = 0; J <= I; ++J) prow[J] /= (double)(i1 - i0);
+    }
+    free(s);
+    free(qi);
+  }
+#ifdef _OPENMP
+  nthreads_used = omp_get_max_threads();
+#endif
+  return 0;
+}
+
 /* Max-based dynamic threshold plus structural blocks, then compaction.
  * P: [hq][nb][nb] (only J <= I is read) or NULL when user_mask is given;
  * user_mask: optional [hq][nb][nb], replaces the threshold and the forced

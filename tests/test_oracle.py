@@ -197,6 +197,73 @@ def test_mask_nesting_in_gamma_and_forced_blocks():
                 assert idx[h, I, :cnt[h, I]].tolist() == np.flatnonzero(m[h, I]).tolist()
 
 
+# ---------------------------------------------------------------- arithmetic scorer
+def test_score_arith_block1_is_causal_attention_probabilities():
+    """With one token per block, the block average is the token itself and
+    pooled keys are the keys: the scorer is textbook causal softmax."""
+    rng = np.random.default_rng(5)
+    hq, hkv, seq, d = 4, 2, 40, 8
+    q = rng.standard_normal((hq, seq, d)).astype(np.float32)
+    k = rng.standard_normal((hkv, seq, d)).astype(np.float32)
+    c = 0.37
+    P = oracle.score_arith(q, k, "f32", 1, c, hkv)
+    L = brute.dense_logits(q.astype(np.float64), k.astype(np.float64), hq, hkv, c)
+    L = np.where(np.tril(np.ones((seq, seq), bool))[None], L, -np.inf)
+    e = np.exp(L - L.max(-1, keepdims=True))
+    np.testing.assert_allclose(P, e / e.sum(-1, keepdims=True), rtol=1e-12, atol=1e-15)
+
+
+def test_score_arith_rows_sum_to_one_with_ragged_tail():
+    c = small_case("bf16", seq=250, block=32, seed=3)
+    P = oracle.score_arith(c.q, c.k, c.dtype, c.block, brute.sm(c.d), c.hkv)
+    nb = P.shape[1]
+    np.testing.assert_allclose(P.sum(-1), 1.0, rtol=0, atol=1e-12)
+    assert np.all(P[:, np.triu_indices(nb, 1)[0], np.triu_indices(nb, 1)[1]] == 0)
+    assert np.all(P >= 0)
+
+
+def test_score_arith_bounds_the_geometric_mean_and_meets_it_for_equal_queries():
+    """The block score is the arithmetic mean of the queries' probabilities;
+    their geometric mean is exp(c Qbar.Kbar_J - mean_i LSE_i) (the pooled-query
+    reading), so the scorer is never below it, and equal for equal queries."""
+    c = small_case("f32", hq=2, hkv=1, seq=256, d=16, block=32, seed=4)
+    cs = brute.sm(c.d)
+    q = brute.decode(c.q, "f32")
+    kb = oracle.pool(c.k, "f32", c.block)
+    P = oracle.score_arith(c.q, c.k, "f32", c.block, cs, c.hkv)
+    nb = kb.shape[1]
+    for h in range(2):
+        for I in range(nb):
+            qi = q[h, I * c.block:(I + 1) * c.block]
+            s = cs * qi @ kb[0, :I + 1].T
+            lse = np.log(np.exp(s - s.max(1, keepdims=True)).sum(1)) + s.max(1)
+            gm = np.exp((s - lse[:, None]).mean(0))
+            assert np.all(gm <= P[h, I, :I + 1] * (1 + 1e-12))
+    # every query of a block equal to the block mean: arithmetic = pooled score
+    qe = c.q.copy()
+    for I in range(nb):
+        qe[:, I * c.block:(I + 1) * c.block] = qe[:, I * c.block:(I + 1) * c.block].mean(1,
+                                                                                         keepdims=True)
+    Pe = oracle.score_arith(qe, c.k, "f32", c.block, cs, c.hkv)
+    _, Pp = oracle.score(oracle.pool(qe, "f32", c.block), kb, cs)
+    np.testing.assert_allclose(Pe, Pp, rtol=1e-9, atol=1e-13)
+
+
+def test_score_arith_fp8_equals_f32_on_dequantised_and_rows_subset():
+    c = small_case("fp8", seq=256, block=64, seed=6)
+    cs = brute.sm(c.d)
+    P8 = oracle.score_arith(c.q, c.k, "fp8", c.block, cs, c.hkv, c.q_scale, c.k_scale)
+    qf = brute.decode(c.q, "fp8", c.q_scale).astype(np.float32)
+    kf = brute.decode(c.k, "fp8", c.k_scale).astype(np.float32)
+    Pf = oracle.score_arith(qf, kf, "f32", c.block, cs, c.hkv)
+    np.testing.assert_allclose(P8, Pf, rtol=1e-6, atol=1e-9)  # f32 rounding of code * scale
+    rows = np.array([0, 3, 5, 9], np.int64)
+    nb = P8.shape[1]
+    np.testing.assert_array_equal(
+        oracle.score_arith(c.q, c.k, "fp8", c.block, cs, c.hkv, c.q_scale, c.k_scale, rows=rows),
+        P8.reshape(-1, nb)[rows])
+
+
 def _exact_calibration(P, target, sink, local):
     """Exhaustive answer: density only changes at the ratios P / row max, so
     the largest gamma with density >= target is the largest such ratio (or 1)
