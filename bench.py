@@ -54,6 +54,9 @@ def parse():
                    help="planted strengths scaled by d**0.25 (logit units): the threshold prunes")
     p.add_argument("--user-density", type=float, default=None,
                    help="replace the scorer by a random caller mask of this density")
+    p.add_argument("--scorer", choices=("pooled", "arith"), default="pooled",
+                   help="stage 1: pooled queries (bsp_score) or the per-query block "
+                        "approximation (bsp_score_arith)")
     p.add_argument("--calibrate", type=float, default=None, metavar="TARGET",
                    help="also time bsp_calibrate_gamma for this target density")
     p.add_argument("--copy-calibration", action="store_true",
@@ -182,7 +185,9 @@ def main():
     def step(ev=None):
         if ev:
             ev[0].record(stream)
-        if um is None:
+        if um is None and a.scorer == "arith":
+            bsp._check(bsp.bsp_score_arith(dsc, P(q), P(k), P(kp), P(sc), sp))
+        elif um is None:
             bsp._check(bsp.bsp_score(dsc, P(q), P(k), P(qp), P(kp), P(sc), sp))
         if ev:
             ev[1].record(stream)
@@ -218,7 +223,13 @@ def main():
     achieved = F_kept / (st_attn * 1e-3) / 1e12
     es = {"f32": 4, "bf16": 2, "fp8": 1}[c.dtype]
     scoring = None
-    if um is None:  # with a caller mask the scorer does not run
+    if um is None and a.scorer == "arith":
+        # one exact product per (query, causal key block) pair: 2 d flops
+        nq = np.minimum(B, seq - np.arange(nb) * B).astype(np.float64)
+        f = 2.0 * d * hq * float((nq * (np.arange(nb) + 1)).sum())
+        scoring = {"scorer": "arith", "flops": f,
+                   "TFLOP/s": round(f / (st_score * 1e-3) / 1e12, 3)}
+    elif um is None:  # with a caller mask the scorer does not run
         sbytes = scoring_bytes(hq, hkv, seq, d, B, es, kept_entries)
         score_gbs = sbytes / ((st_score + st_mask) * 1e-3) / 1e9
         scoring = {"bytes": sbytes, "GB/s": round(score_gbs, 1),
@@ -244,13 +255,15 @@ def main():
         cpu = cpu_baseline(c, mk.cpu().numpy(), a.cpu_rows)
 
     traffic = traffic_from_note() if (a.config == 3 and a.seq is None and um is None
-                                      and not a.s2) else None
+                                      and not a.s2 and a.scorer == "pooled") else None
     wl = (f"{c.name}: {hq} q / {hkv} kv heads, seq {seq}, d {d}, block {B}, gamma {c.gamma}, "
           f"causal, {c.dtype}, batch 1, one layer")
     if um is not None:
         wl += f", caller mask density {a.user_density}"
     if a.s2:
         wl += ", planted strengths in logit units (x d^0.25)"
+    if a.scorer == "arith":
+        wl += ", per-query block-approximation scorer"
     out = {
         "metric": "sparse prefill-attn ms/layer + effective TFLOP/s at 128K bf16; % MFMA peak",
         "value": round(F_dense / (ms_step * 1e-3) / 1e12, 3),

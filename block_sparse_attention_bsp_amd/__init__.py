@@ -20,7 +20,8 @@ import torch
 
 __all__ = [
     "BspError", "BspDesc", "lib", "library_path", "desc", "score", "mask", "attn_fwd", "prefill",
-    "calibrate_gamma", "bsp_score", "bsp_mask", "bsp_attn_fwd", "bsp_calibrate_gamma",
+    "calibrate_gamma", "score_arith", "bsp_score", "bsp_score_arith", "bsp_mask", "bsp_attn_fwd",
+    "bsp_calibrate_gamma",
     "bsp_status_string", "bsp_abi_version",
     "DTYPE_F32", "DTYPE_BF16", "DTYPE_FP8_E4M3",
 ]
@@ -65,11 +66,13 @@ def lib():
         vp, P = ctypes.c_void_p, ctypes.POINTER(BspDesc)
         L.bsp_score.argtypes = [P, vp, vp, vp, vp, vp, vp]
         L.bsp_mask.argtypes = [P, vp, vp, vp, vp, vp, vp]
+        L.bsp_score_arith.argtypes = [P, vp, vp, vp, vp, vp]
         L.bsp_attn_fwd.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp]
         f32 = ctypes.c_float
         L.bsp_calibrate_gamma.argtypes = [P, vp, f32, f32, vp, vp, vp, vp,
                                           ctypes.POINTER(f32), ctypes.POINTER(f32), vp]
-        for f in (L.bsp_score, L.bsp_mask, L.bsp_attn_fwd, L.bsp_calibrate_gamma):
+        for f in (L.bsp_score, L.bsp_score_arith, L.bsp_mask, L.bsp_attn_fwd,
+                  L.bsp_calibrate_gamma):
             f.restype = ctypes.c_int32
         L.bsp_status_string.argtypes = [ctypes.c_int32]
         L.bsp_status_string.restype = ctypes.c_char_p
@@ -94,6 +97,10 @@ def _check(status: int):
 
 def bsp_score(d: BspDesc, q, k, q_pool, k_pool, score_out, stream) -> int:
     return lib().bsp_score(ctypes.byref(d), q, k, q_pool, k_pool, score_out, stream)
+
+
+def bsp_score_arith(d: BspDesc, q, k, k_pool, score_out, stream) -> int:
+    return lib().bsp_score_arith(ctypes.byref(d), q, k, k_pool, score_out, stream)
 
 
 def bsp_mask(d: BspDesc, score_in, user_mask, mask_out, kv_idx, kv_cnt, stream) -> int:
@@ -180,6 +187,19 @@ def score(q: torch.Tensor, k: torch.Tensor, block: int, sm_scale: float = 0.0,
     sc = torch.empty((hq, nb, nb), dtype=torch.float32, device=q.device)
     _check(bsp_score(dsc, _ptr(q), _ptr(k), _ptr(qp), _ptr(kp), _ptr(sc), _stream()))
     return qp, kp, sc
+
+
+def score_arith(q: torch.Tensor, k: torch.Tensor, block: int, sm_scale: float = 0.0,
+                q_scale=None, k_scale=None):
+    """Stage 1 with the per-query block approximation.  Returns
+    (k_pool [hkv,nb,d], score [hq,nb,nb]) fp32."""
+    dsc = _desc_qkv(q, k, block, sm_scale=sm_scale, q_scale=q_scale, k_scale=k_scale)
+    hq, seq, d = q.shape
+    nb = -(-seq // block)
+    kp = torch.empty((k.shape[0], nb, d), dtype=torch.float32, device=q.device)
+    sc = torch.empty((hq, nb, nb), dtype=torch.float32, device=q.device)
+    _check(bsp_score_arith(dsc, _ptr(q), _ptr(k), _ptr(kp), _ptr(sc), _stream()))
+    return kp, sc
 
 
 def mask(score_t: Optional[torch.Tensor], gamma: float, seq: int, block: int,

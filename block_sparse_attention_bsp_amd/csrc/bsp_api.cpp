@@ -64,6 +64,24 @@ bsp_status bsp_score(const bsp_desc *desc, const void *q, const void *k, float *
   return hip_status(bsp::launch_score(s, scale_of(desc), q_pool, k_pool, score, hs));
 }
 
+bsp_status bsp_score_arith(const bsp_desc *desc, const void *q, const void *k, float *k_pool,
+                           float *score, void *stream) {
+  bsp_status st = check_desc(desc, true);
+  if (st != BSP_OK) return st;
+  if (desc->seq == 0) return BSP_OK;
+  if (!q || !k || !k_pool || !score) return BSP_ERR_NULL_POINTER;
+  const bool fp8 = desc->dtype == BSP_DTYPE_FP8_E4M3;
+  if (fp8 && (!desc->q_scale || !desc->k_scale)) return BSP_ERR_BAD_DTYPE;
+  if (!fp8 && (desc->q_scale || desc->k_scale || desc->v_scale)) return BSP_ERR_BAD_DTYPE;
+  Shape s = shape_of(desc);
+  hipStream_t hs = (hipStream_t)stream;
+  Shape sk = s;
+  sk.hq = 0;  // keys only
+  if (bsp::launch_pool(sk, nullptr, k, nullptr, desc->k_scale, nullptr, k_pool, hs) != hipSuccess)
+    return BSP_ERR_HIP;
+  return hip_status(bsp::launch_score_arith(s, scale_of(desc), q, k_pool, score, desc->q_scale, hs));
+}
+
 bsp_status bsp_mask(const bsp_desc *desc, const float *score, const uint8_t *user_mask,
                     uint8_t *mask, int32_t *kv_idx, int32_t *kv_cnt, void *stream) {
   bsp_status st = check_desc(desc, false);

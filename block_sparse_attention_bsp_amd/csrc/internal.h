@@ -24,6 +24,8 @@ hipError_t launch_pool(const Shape &s, const void *q, const void *k, const float
                        const float *k_scale, float *q_pool, float *k_pool, hipStream_t st);
 hipError_t launch_score(const Shape &s, float c, const float *q_pool, const float *k_pool,
                         float *score, hipStream_t st);
+hipError_t launch_score_arith(const Shape &s, float c, const void *q, const float *k_pool,
+                              float *score, const float *q_scale, hipStream_t st);
 hipError_t launch_mask(const Shape &s, float gamma, int sink_blocks, int local_blocks,
                        const float *score, const uint8_t *user_mask, uint8_t *mask,
                        int32_t *kv_idx, int32_t *kv_cnt, hipStream_t st);

@@ -44,7 +44,7 @@
 extern "C" {
 #endif
 
-#define BSP_ABI_VERSION 2
+#define BSP_ABI_VERSION 3
 
 typedef enum bsp_status {
   BSP_OK = 0,
@@ -103,6 +103,28 @@ typedef struct bsp_desc {
  */
 bsp_status bsp_score(const bsp_desc *desc, const void *q, const void *k, float *q_pool,
                      float *k_pool, float *score, void *stream);
+
+/*
+ * bsp_score_arith - stage 1 with the per-query block approximation (section
+ * 3 "Instantaneous Pattern Discovery": pooled key blocks stand in for their
+ * tokens and a block's significance is the average over its queries; "Block
+ * Approximation for Kernel Optimization": a single fused pass on the
+ * (L/B) x (L/B) grid, no L x (L/B) intermediate).  Kbar as in bsp_score;
+ * for J <= I
+ *   score[h][I][J] = mean over the valid tokens i of block I of
+ *                    exp(c * q_i . Kbar[g][J]) / sum_{J' <= I} exp(c * q_i . Kbar[g][J'])
+ * and 0 for J > I; every row sums to 1.  q_i is dequantised (times
+ * q_scale[h]) for fp8.  The result feeds bsp_mask like bsp_score's.
+ * Arithmetic: fp32-accurate scores (fp32 MFMA for fp32 inputs; otherwise bf16
+ * MFMA on exact queries against an exact three-way bf16 split of Kbar).
+ *
+ * q, k:    device, storage dtype, [hq][seq][d] and [hkv][seq][d]
+ * k_pool:  device float [hkv][nb][d]    (written)
+ * score:   device float [hq][nb][nb]    (written, every entry)
+ * Needs desc->q_scale and desc->k_scale for fp8 (v_scale is not read).
+ */
+bsp_status bsp_score_arith(const bsp_desc *desc, const void *q, const void *k, float *k_pool,
+                           float *score, void *stream);
 
 /*
  * bsp_mask - stage 2, max-based dynamic thresholding and block selection

@@ -28,7 +28,7 @@ def built():
 
 def test_header_declares_the_entry_points():
     assert _declared() == ["bsp_abi_version", "bsp_attn_fwd", "bsp_calibrate_gamma", "bsp_mask",
-                           "bsp_score", "bsp_status_string"]
+                           "bsp_score", "bsp_score_arith", "bsp_status_string"]
 
 
 def test_library_exports_every_declared_symbol():

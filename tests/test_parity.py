@@ -128,6 +128,42 @@ def test_long_kv_lists(dtype):
     print(f"  max-abs O err {err:.2e}", flush=True)
 
 
+def _arith_case(which):
+    if which.startswith("s1_"):
+        return gen.make_s1(int(which[-1]))
+    if which == "llama_4k":
+        return gen.make_config(1)
+    if which == "qwen_4k_fp8":
+        return gen.make_config(4, seq=4096)
+    dtype, d, block, seq = which.split("_")
+    return gen.make_case(8, 2, int(seq), int(d), int(block), dtype, 7 + int(seq), gamma=0.2,
+                         rope=True, n_vert=6, slash=True, block_offset=1.0)
+
+
+@pytest.mark.parametrize("which", ["s1_0", "s1_3", "bf16_128_128_1000", "bf16_64_64_777",
+                                   "fp8_128_128_1000", "fp8_64_64_700", "f32_128_64_333",
+                                   "f32_64_128_250", "llama_4k", "qwen_4k_fp8"])
+def test_score_arith_matches_oracle(which):
+    """Per-query block-approximation scores and the mask built on them."""
+    announce(f"arithmetic scorer {which}")
+    c = _arith_case(which)
+    d = H.dev(c)
+    kp, sc = bsp.score_arith(d["q"], d["k"], c.block, q_scale=d["q_scale"], k_scale=d["k_scale"])
+    g = c.gamma
+    m, idx, cnt = bsp.mask(sc, g, c.seq, c.block)
+    torch.cuda.synchronize()
+    cs = 1.0 / math.sqrt(c.d)
+    P = oracle.score_arith(c.q, c.k, c.dtype, c.block, cs, c.hkv, c.q_scale, c.k_scale)
+    np.testing.assert_allclose(kp.cpu().numpy(), oracle.pool(c.k, c.dtype, c.block, c.k_scale),
+                               rtol=1e-5, atol=2e-6)
+    np.testing.assert_allclose(sc.cpu().numpy(), P, rtol=1e-4, atol=1e-6)
+    om, oidx, ocnt = oracle.mask(P, g)
+    nband = H.check_mask(m.cpu().numpy(), idx.cpu().numpy(), cnt.cpu().numpy(),
+                         dict(P=P, mask=om, idx=oidx, cnt=ocnt), g)
+    dens = om.sum() / (c.hq * c.nb * (c.nb + 1) / 2)
+    print(f"  density {dens:.3f} band blocks {nband}", flush=True)
+
+
 @pytest.mark.parametrize("which,target", [("s1_0", 0.3), ("s1_1", 0.7), ("llama_4k", 0.7)])
 def test_calibrate_gamma_matches_oracle(which, target):
     """Bisection on the GPU masks lands on the oracle's gamma; the buffers
