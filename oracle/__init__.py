@@ -47,6 +47,9 @@ def lib():
         L.oracle_pool.argtypes = [i32, i32, i32, i32, i32, vp, vp, vp]
         L.oracle_score.argtypes = [i32, i32, i32, i32, vp, vp, dbl, vp, vp]
         L.oracle_mask.argtypes = [i32, i32, vp, vp, dbl, i32, i32, vp, vp, vp]
+        L.oracle_key_radius.argtypes = [i32, i32, i32, i32, i32, vp, vp, vp, vp]
+        L.oracle_score_rescue.argtypes = [i32, i32, i32, i32, vp, vp, vp, dbl, vp, vp]
+        L.oracle_mask_dual.argtypes = [i32, i32, vp, vp, dbl, dbl, i32, i32, vp, vp, vp]
         L.oracle_score_arith.argtypes = [i32, i32, i32, i32, i32, i32, vp, vp, vp, dbl,
                                          ctypes.c_long, vp, vp]
         L.oracle_attn.argtypes = [i32, i32, i32, i32, i32, i32, vp, vp, vp, vp, vp, vp, dbl,
@@ -120,6 +123,46 @@ def score_arith(q: np.ndarray, k: np.ndarray, dtype: str, block: int, c: float, 
     lib().oracle_score_arith(hq, hkv, seq, d, block, _DT[dtype], _p(q),
                              _p(_c(q_scale, np.float32)), _p(kbar), float(c), n, _p(r), _p(out))
     return out.reshape(hq, nb, nb) if r is None else out
+
+
+def key_radius(k: np.ndarray, dtype: str, block: int, k_scale=None) -> np.ndarray:
+    """[hkv, nb]: max distance of a block's keys from their mean (the
+    rescue-branch radius; see oracle_key_radius)."""
+    k = np.ascontiguousarray(k)
+    hkv, seq, d = k.shape
+    kbar = pool(k, dtype, block, k_scale)
+    r = np.empty((hkv, kbar.shape[1]), np.float64)
+    lib().oracle_key_radius(hkv, seq, d, block, _DT[dtype], _p(k), _p(_c(k_scale, np.float32)),
+                            _p(kbar), _p(r))
+    return r
+
+
+def score_rescue(qbar: np.ndarray, kbar: np.ndarray, radius: np.ndarray, c: float):
+    """Rescue scores R = c (Qbar.Kbar + |Qbar| r) and their row softmax Pr,
+    both [hq, nb, nb], zero above the diagonal."""
+    qbar = _c(qbar, np.float64)
+    kbar = _c(kbar, np.float64)
+    hq, nb, d = qbar.shape
+    R = np.empty((hq, nb, nb), np.float64)
+    Pr = np.empty((hq, nb, nb), np.float64)
+    lib().oracle_score_rescue(hq, kbar.shape[0], nb, d, _p(qbar), _p(kbar),
+                              _p(_c(radius, np.float64)), float(c), _p(R), _p(Pr))
+    return R, Pr
+
+
+def mask_dual(P: np.ndarray, Pr: np.ndarray, gamma: float, gamma_r: float, sink_blocks: int = 1,
+              local_blocks: int = 1):
+    """Base and rescue branches thresholded independently and combined.
+    Returns (mask, idx (-1 past cnt), cnt)."""
+    P = _c(P, np.float64)
+    Pr = _c(Pr, np.float64)
+    hq, nb, _ = P.shape
+    m = np.empty((hq, nb, nb), np.uint8)
+    idx = np.empty((hq, nb, nb), np.int32)
+    cnt = np.empty((hq, nb), np.int32)
+    lib().oracle_mask_dual(hq, nb, _p(P), _p(Pr), float(gamma), float(gamma_r), sink_blocks,
+                           local_blocks, _p(m), _p(idx), _p(cnt))
+    return m, idx, cnt
 
 
 def mask(P: Optional[np.ndarray], gamma: float, sink_blocks: int = 1, local_blocks: int = 1,

@@ -312,3 +312,99 @@ int oracle_attn(int hq, int hkv, int seq, int d, int block, int dtype, const voi
   (void)nb;
   return 0;
 }
+
+/* ---------------------------------------------------------------- rescue
+ * Radius-based rescue branch (thelatestinai page, RBS-Attention abstract: a
+ * centroid base branch plus a rescue branch built on the maximum key-block
+ * radius, each thresholded on its own, masks combined).  The page gives no
+ * formula; the reading taken here:
+ *   radius  r[g][J] = max over the valid keys k of block J of ||k - Kbar_J||
+ *   rescue  R[h][I][J] = c * (Qbar_I . Kbar_J + ||Qbar_I|| * r[g][J]),
+ *           an upper bound on c * Qbar_I . k for every key k of block J
+ *           (Cauchy-Schwarz), row-softmaxed over J <= I like the base score;
+ *   mask    keep = causal AND (base keep OR rescue keep OR forced), each
+ *           branch with its own max-based threshold factor. */
+
+/* k: [hkv][seq][d] storage values (fp8 codes times k_scale[g]); kbar from
+ * oracle_pool on the same keys.  r: [hkv][nb]. */
+int oracle_key_radius(int hkv, int seq, int d, int block, int dtype, const void *k,
+                      const float *k_scale, const double *kbar, double *r) {
+  init_tables();
+  int nb = (seq + block - 1) / block;
+#pragma omp parallel for collapse(2) schedule(static)
+  for (int g = 0; g < hkv; ++g)
+    for (int J = 0; J < nb; ++J) {
+      double s = k_scale ? (double)k_scale[g] : 1.0, best = 0.0;
+      const double *m = kbar + ((size_t)g * nb + J) * d;
+      int t1 = (J + 1) * block < seq ? (J + 1) * block : seq;
+      for (int t = J * block; t < t1; ++t) {
+        double d2 = 0.0;
+        for (int e = 0; e < d; ++e) {
+          double x = load(k, dtype, ((size_t)g * seq + t) * d + e) * s - m[e];
+          d2 += x * x;
+        }
+        if (d2 > best) best = d2;
+      }
+      r[(size_t)g * nb + J] = sqrt(best);
+    }
+  return 0;
+}
+
+/* qbar [hq][nb][d], kbar [hkv][nb][d], r [hkv][nb] -> rescue scores and
+ * their row softmax, [hq][nb][nb], 0 above the diagonal (R may be NULL). */
+int oracle_score_rescue(int hq, int hkv, int nb, int d, const double *qbar, const double *kbar,
+                        const double *r, double c, double *R, double *Pr) {
+  int grp = hq / hkv;
+#pragma omp parallel for collapse(2) schedule(dynamic, 4)
+  for (int h = 0; h < hq; ++h)
+    for (int I = 0; I < nb; ++I) {
+      int g = h / grp;
+      const double *qi = qbar + ((size_t)h * nb + I) * d;
+      double *prow = Pr + ((size_t)h * nb + I) * nb;
+      double qn = 0.0, m = -INFINITY, l = 0.0;
+      for (int e = 0; e < d; ++e) qn += qi[e] * qi[e];
+      qn = sqrt(qn);
+      for (int J = 0; J < nb; ++J) prow[J] = 0.0;
+      for (int J = 0; J <= I; ++J) {
+        const double *kj = kbar + ((size_t)g * nb + J) * d;
+        double dot = 0.0;
+        for (int e = 0; e < d; ++e) dot += qi[e] * kj[e];
+        prow[J] = c * (dot + qn * r[(size_t)g * nb + J]);
+        if (prow[J] > m) m = prow[J];
+      }
+      if (R) {
+        double *rrow = R + ((size_t)h * nb + I) * nb;
+        for (int J = 0; J < nb; ++J) rrow[J] = J <= I ? prow[J] : 0.0;
+      }
+      for (int J = 0; J <= I; ++J) l += exp(prow[J] - m);
+      for (int J = 0; J <= I; ++J) prow[J] = exp(prow[J] - m) / l;
+    }
+  return 0;
+}
+
+/* Both branches thresholded independently, then combined with the forced
+ * blocks and the causal condition; compaction as in oracle_mask. */
+int oracle_mask_dual(int hq, int nb, const double *P, const double *Pr, double gamma,
+                     double gamma_r, int sink_blocks, int local_blocks, uint8_t *mask,
+                     int32_t *idx, int32_t *cnt) {
+#pragma omp parallel for collapse(2) schedule(static)
+  for (int h = 0; h < hq; ++h)
+    for (int I = 0; I < nb; ++I) {
+      size_t row = (size_t)h * nb + I;
+      double pmax = -INFINITY, rmax = -INFINITY;
+      for (int J = 0; J <= I; ++J) {
+        if (P[row * nb + J] > pmax) pmax = P[row * nb + J];
+        if (Pr[row * nb + J] > rmax) rmax = Pr[row * nb + J];
+      }
+      int n = 0;
+      for (int J = 0; J < nb; ++J) {
+        int keep = J <= I && (P[row * nb + J] >= gamma * pmax || Pr[row * nb + J] >= gamma_r * rmax ||
+                              J < sink_blocks || I - J < local_blocks);
+        mask[row * nb + J] = (uint8_t)keep;
+        if (keep) idx[row * nb + n++] = J;
+      }
+      for (int J = n; J < nb; ++J) idx[row * nb + J] = -1;
+      cnt[row] = n;
+    }
+  return 0;
+}

@@ -264,6 +264,83 @@ def test_score_arith_fp8_equals_f32_on_dequantised_and_rows_subset():
         P8.reshape(-1, nb)[rows])
 
 
+# ---------------------------------------------------------------- rescue branch
+def test_key_radius_closed_forms():
+    rng = np.random.default_rng(11)
+    hkv, block, d = 2, 16, 8
+    seq = 5 * block + 6  # ragged tail of 6 keys
+    k = np.empty((hkv, seq, d), np.float32)
+    a = rng.standard_normal((hkv, 6, d)).astype(np.float32)
+    b = rng.standard_normal((hkv, 6, d)).astype(np.float32)
+    for J in range(6):
+        t0, t1 = J * block, min((J + 1) * block, seq)
+        n = t1 - t0
+        k[:, t0:t1] = a[:, J:J + 1]
+        if J % 2:  # two-point block: half the keys at a, half at b
+            k[:, t0 + n // 2:t1] = b[:, J:J + 1]
+    r = oracle.key_radius(k, "f32", block)
+    for J in range(6):
+        want = 0.0 if J % 2 == 0 else np.linalg.norm(a[:, J].astype(np.float64) - b[:, J], axis=-1) / 2
+        np.testing.assert_allclose(r[:, J], want, rtol=1e-6, atol=1e-6)
+    # translating every key of a block leaves its radius unchanged
+    x = rng.standard_normal((hkv, 4 * block, d)).astype(np.float32)
+    r1 = oracle.key_radius(x, "f32", block)
+    r2 = oracle.key_radius(x + np.float32(3.0), "f32", block)
+    np.testing.assert_allclose(r1, r2, rtol=1e-5)
+
+
+def test_rescue_score_bounds_every_key_and_is_tight_along_the_query():
+    c = small_case("f32", hq=2, hkv=1, seq=128, d=8, block=16, seed=12)
+    cs = brute.sm(c.d)
+    qb = oracle.pool(c.q, "f32", c.block)
+    kb = oracle.pool(c.k, "f32", c.block)
+    r = oracle.key_radius(c.k, "f32", c.block)
+    R, Pr = oracle.score_rescue(qb, kb, r, cs)
+    k = brute.decode(c.k, "f32")
+    nb = qb.shape[1]
+    for h in range(2):
+        for I in range(nb):
+            for J in range(I + 1):
+                best = (cs * k[0, J * c.block:(J + 1) * c.block] @ qb[h, I]).max()
+                assert R[h, I, J] >= best - 1e-9
+    np.testing.assert_allclose(Pr.sum(-1), 1.0, atol=1e-12)
+    # keys of block 2 at its mean +- t * u, u along Qbar of row (0, 5): the bound is reached
+    k2 = c.k.copy()
+    u = qb[0, 5] / np.linalg.norm(qb[0, 5])
+    mvec = kb[0, 2]
+    t = 0.75
+    k2[0, 2 * c.block:3 * c.block:2] = (mvec + t * u).astype(np.float32)
+    k2[0, 2 * c.block + 1:3 * c.block:2] = (mvec - t * u).astype(np.float32)
+    kb2 = oracle.pool(k2, "f32", c.block)
+    r2 = oracle.key_radius(k2, "f32", c.block)
+    R2, _ = oracle.score_rescue(qb, kb2, r2, cs)
+    best = (cs * brute.decode(k2, "f32")[0, 2 * c.block:3 * c.block] @ qb[0, 5]).max()
+    np.testing.assert_allclose(R2[0, 5, 2], best, rtol=1e-6)
+
+
+def test_mask_dual_union_and_zero_radius_reduction():
+    c = gen.make_s1(2)
+    cs = brute.sm(c.d)
+    qb = oracle.pool(c.q, c.dtype, c.block)
+    kb = oracle.pool(c.k, c.dtype, c.block)
+    _, P = oracle.score(qb, kb, cs)
+    r = oracle.key_radius(c.k, c.dtype, c.block)
+    _, Pr = oracle.score_rescue(qb, kb, r, cs)
+    for g, gr in [(0.1, 0.3), (0.3, 0.05), (1.0, 1.0)]:
+        m, idx, cnt = oracle.mask_dual(P, Pr, g, gr)
+        mb = oracle.mask(P, g)[0]
+        mr = oracle.mask(Pr, gr)[0]
+        assert np.array_equal(m, mb | mr)
+        for h in range(c.hq):
+            for I in range(c.nb):
+                assert idx[h, I, :cnt[h, I]].tolist() == np.flatnonzero(m[h, I]).tolist()
+    # no radius: the rescue branch is the base score, the union is the laxer threshold
+    _, P0 = oracle.score_rescue(qb, kb, np.zeros_like(r), cs)
+    np.testing.assert_allclose(P0, P, rtol=1e-12, atol=1e-15)
+    for g, gr in [(0.1, 0.4), (0.5, 0.2)]:
+        assert np.array_equal(oracle.mask_dual(P, P0, g, gr)[0], oracle.mask(P, min(g, gr))[0])
+
+
 def _exact_calibration(P, target, sink, local):
     """Exhaustive answer: density only changes at the ratios P / row max, so
     the largest gamma with density >= target is the largest such ratio (or 1)
