@@ -57,6 +57,9 @@ def parse():
     p.add_argument("--scorer", choices=("pooled", "arith"), default="pooled",
                    help="stage 1: pooled queries (bsp_score) or the per-query block "
                         "approximation (bsp_score_arith)")
+    p.add_argument("--rescue", type=float, default=None, metavar="GAMMA_R",
+                   help="add the radius-based rescue branch (bsp_score_rescue + bsp_mask_dual) "
+                        "with this threshold factor")
     p.add_argument("--calibrate", type=float, default=None, metavar="TARGET",
                    help="also time bsp_calibrate_gamma for this target density")
     p.add_argument("--copy-calibration", action="store_true",
@@ -171,6 +174,9 @@ def main():
     qp = torch.empty((hq, nb, d), dtype=f32, device=dev)
     kp = torch.empty((hkv, nb, d), dtype=f32, device=dev)
     sc = torch.empty((hq, nb, nb), dtype=f32, device=dev)
+    resc = a.rescue is not None and a.user_density is None
+    kr = torch.empty((hkv, nb), dtype=f32, device=dev) if resc else None
+    rs = torch.empty((hq, nb, nb), dtype=f32, device=dev) if resc else None
     mk = torch.empty((hq, nb, nb), dtype=torch.uint8, device=dev)
     idx = torch.empty((hq, nb, nb), dtype=torch.int32, device=dev)
     cnt = torch.empty((hq, nb), dtype=torch.int32, device=dev)
@@ -189,10 +195,15 @@ def main():
             bsp._check(bsp.bsp_score_arith(dsc, P(q), P(k), P(kp), P(sc), sp))
         elif um is None:
             bsp._check(bsp.bsp_score(dsc, P(q), P(k), P(qp), P(kp), P(sc), sp))
+        if resc:
+            bsp._check(bsp.bsp_score_rescue(dsc, P(k), P(qp), P(kp), P(kr), P(rs), sp))
         if ev:
             ev[1].record(stream)
-        bsp._check(bsp.bsp_mask(dsc, None if um is not None else P(sc), P(um), P(mk), P(idx),
-                                P(cnt), sp))
+        if resc:
+            bsp._check(bsp.bsp_mask_dual(dsc, P(sc), P(rs), a.rescue, P(mk), P(idx), P(cnt), sp))
+        else:
+            bsp._check(bsp.bsp_mask(dsc, None if um is not None else P(sc), P(um), P(mk), P(idx),
+                                    P(cnt), sp))
         if ev:
             ev[2].record(stream)
         bsp._check(bsp.bsp_attn_fwd(dsc, P(q), P(k), P(v), P(idx), P(cnt), P(o), P(lse), sp))
@@ -231,6 +242,9 @@ def main():
                    "TFLOP/s": round(f / (st_score * 1e-3) / 1e12, 3)}
     elif um is None:  # with a caller mask the scorer does not run
         sbytes = scoring_bytes(hq, hkv, seq, d, B, es, kept_entries)
+        if resc:  # K again, the means again, radii, rescue scores written and half read
+            sbytes += (hkv * seq * d * es + (hq + 2 * hkv) * nb * d * 4 + 2 * hkv * nb * 4
+                       + hq * nb * nb * 4 + hq * nb * (nb + 1) // 2 * 4)
         score_gbs = sbytes / ((st_score + st_mask) * 1e-3) / 1e9
         scoring = {"bytes": sbytes, "GB/s": round(score_gbs, 1),
                    "hbm_frac": round(score_gbs / PEAK_HBM_GBS, 4)}
@@ -255,7 +269,8 @@ def main():
         cpu = cpu_baseline(c, mk.cpu().numpy(), a.cpu_rows)
 
     traffic = traffic_from_note() if (a.config == 3 and a.seq is None and um is None
-                                      and not a.s2 and a.scorer == "pooled") else None
+                                      and not a.s2 and a.scorer == "pooled"
+                                      and not resc) else None
     wl = (f"{c.name}: {hq} q / {hkv} kv heads, seq {seq}, d {d}, block {B}, gamma {c.gamma}, "
           f"causal, {c.dtype}, batch 1, one layer")
     if um is not None:
@@ -264,6 +279,8 @@ def main():
         wl += ", planted strengths in logit units (x d^0.25)"
     if a.scorer == "arith":
         wl += ", per-query block-approximation scorer"
+    if resc:
+        wl += f", rescue branch gamma_r {a.rescue}"
     out = {
         "metric": "sparse prefill-attn ms/layer + effective TFLOP/s at 128K bf16; % MFMA peak",
         "value": round(F_dense / (ms_step * 1e-3) / 1e12, 3),

@@ -20,8 +20,8 @@ import torch
 
 __all__ = [
     "BspError", "BspDesc", "lib", "library_path", "desc", "score", "mask", "attn_fwd", "prefill",
-    "calibrate_gamma", "score_arith", "bsp_score", "bsp_score_arith", "bsp_mask", "bsp_attn_fwd",
-    "bsp_calibrate_gamma",
+    "calibrate_gamma", "score_arith", "score_rescue", "mask_dual", "bsp_score", "bsp_score_arith",
+    "bsp_score_rescue", "bsp_mask", "bsp_mask_dual", "bsp_attn_fwd", "bsp_calibrate_gamma",
     "bsp_status_string", "bsp_abi_version",
     "DTYPE_F32", "DTYPE_BF16", "DTYPE_FP8_E4M3",
 ]
@@ -67,12 +67,14 @@ def lib():
         L.bsp_score.argtypes = [P, vp, vp, vp, vp, vp, vp]
         L.bsp_mask.argtypes = [P, vp, vp, vp, vp, vp, vp]
         L.bsp_score_arith.argtypes = [P, vp, vp, vp, vp, vp]
+        L.bsp_score_rescue.argtypes = [P, vp, vp, vp, vp, vp, vp]
+        L.bsp_mask_dual.argtypes = [P, vp, vp, ctypes.c_float, vp, vp, vp, vp]
         L.bsp_attn_fwd.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp]
         f32 = ctypes.c_float
         L.bsp_calibrate_gamma.argtypes = [P, vp, f32, f32, vp, vp, vp, vp,
                                           ctypes.POINTER(f32), ctypes.POINTER(f32), vp]
-        for f in (L.bsp_score, L.bsp_score_arith, L.bsp_mask, L.bsp_attn_fwd,
-                  L.bsp_calibrate_gamma):
+        for f in (L.bsp_score, L.bsp_score_arith, L.bsp_score_rescue, L.bsp_mask,
+                  L.bsp_mask_dual, L.bsp_attn_fwd, L.bsp_calibrate_gamma):
             f.restype = ctypes.c_int32
         L.bsp_status_string.argtypes = [ctypes.c_int32]
         L.bsp_status_string.restype = ctypes.c_char_p
@@ -101,6 +103,16 @@ def bsp_score(d: BspDesc, q, k, q_pool, k_pool, score_out, stream) -> int:
 
 def bsp_score_arith(d: BspDesc, q, k, k_pool, score_out, stream) -> int:
     return lib().bsp_score_arith(ctypes.byref(d), q, k, k_pool, score_out, stream)
+
+
+def bsp_score_rescue(d: BspDesc, k, q_pool, k_pool, k_radius, rescue_out, stream) -> int:
+    return lib().bsp_score_rescue(ctypes.byref(d), k, q_pool, k_pool, k_radius, rescue_out, stream)
+
+
+def bsp_mask_dual(d: BspDesc, score_in, rescue_in, gamma_rescue: float, mask_out, kv_idx, kv_cnt,
+                  stream) -> int:
+    return lib().bsp_mask_dual(ctypes.byref(d), score_in, rescue_in, gamma_rescue, mask_out,
+                               kv_idx, kv_cnt, stream)
 
 
 def bsp_mask(d: BspDesc, score_in, user_mask, mask_out, kv_idx, kv_cnt, stream) -> int:
@@ -200,6 +212,47 @@ def score_arith(q: torch.Tensor, k: torch.Tensor, block: int, sm_scale: float = 
     sc = torch.empty((hq, nb, nb), dtype=torch.float32, device=q.device)
     _check(bsp_score_arith(dsc, _ptr(q), _ptr(k), _ptr(kp), _ptr(sc), _stream()))
     return kp, sc
+
+
+def score_rescue(k: torch.Tensor, q_pool: torch.Tensor, k_pool: torch.Tensor, seq: int, block: int,
+                 sm_scale: float = 0.0, k_scale=None):
+    """Rescue branch.  Returns (k_radius [hkv,nb], rescue [hq,nb,nb]) fp32."""
+    hq, nb, d = q_pool.shape
+    hkv = k.shape[0]
+    _shape(k, (hkv, seq, d), "k")
+    _shape(k_pool, (hkv, nb, d), "k_pool")
+    _shape(k_scale, (hkv,), "k_scale")
+    if nb != -(-seq // block):
+        raise BspError(2, "q_pool does not match seq and block")
+    for t in (q_pool, k_pool):
+        if t.dtype != torch.float32:
+            raise BspError(3, "q_pool / k_pool must be float32")
+    dsc = desc(hq, hkv, seq, d, block, _dtype_code(k), sm_scale=sm_scale, k_scale=k_scale)
+    kr = torch.empty((hkv, nb), dtype=torch.float32, device=k.device)
+    rs = torch.empty((hq, nb, nb), dtype=torch.float32, device=k.device)
+    _check(bsp_score_rescue(dsc, _ptr(k), _ptr(q_pool), _ptr(k_pool), _ptr(kr), _ptr(rs),
+                            _stream()))
+    return kr, rs
+
+
+def mask_dual(score_t: torch.Tensor, rescue_t: torch.Tensor, gamma: float, gamma_rescue: float,
+              seq: int, block: int, sink_blocks: int = 1, local_blocks: int = 1):
+    """Both branches thresholded and combined.  Returns (mask, kv_idx, kv_cnt)."""
+    hq, nb, _ = score_t.shape
+    if nb != -(-seq // block):
+        raise BspError(2, "score does not match seq and block")
+    for name, t in (("score", score_t), ("rescue", rescue_t)):
+        _shape(t, (hq, nb, nb), name)
+        if t.dtype != torch.float32:
+            raise BspError(3, f"{name} must be float32")
+    dsc = desc(hq, 1, seq, 64, block, DTYPE_F32, gamma=gamma, sink_blocks=sink_blocks,
+               local_blocks=local_blocks)
+    m = torch.empty((hq, nb, nb), dtype=torch.uint8, device=score_t.device)
+    idx = torch.empty((hq, nb, nb), dtype=torch.int32, device=score_t.device)
+    cnt = torch.empty((hq, nb), dtype=torch.int32, device=score_t.device)
+    _check(bsp_mask_dual(dsc, _ptr(score_t), _ptr(rescue_t), gamma_rescue, _ptr(m), _ptr(idx),
+                         _ptr(cnt), _stream()))
+    return m, idx, cnt
 
 
 def mask(score_t: Optional[torch.Tensor], gamma: float, seq: int, block: int,

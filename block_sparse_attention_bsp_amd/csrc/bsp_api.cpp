@@ -61,7 +61,7 @@ bsp_status bsp_score(const bsp_desc *desc, const void *q, const void *k, float *
   hipStream_t hs = (hipStream_t)stream;
   hipError_t e = bsp::launch_pool(s, q, k, desc->q_scale, desc->k_scale, q_pool, k_pool, hs);
   if (e != hipSuccess) return BSP_ERR_HIP;
-  return hip_status(bsp::launch_score(s, scale_of(desc), q_pool, k_pool, score, hs));
+  return hip_status(bsp::launch_score(s, scale_of(desc), q_pool, k_pool, nullptr, score, hs));
 }
 
 bsp_status bsp_score_arith(const bsp_desc *desc, const void *q, const void *k, float *k_pool,
@@ -94,6 +94,38 @@ bsp_status bsp_mask(const bsp_desc *desc, const float *score, const uint8_t *use
   return hip_status(bsp::launch_mask(s, desc->gamma, desc->sink_blocks, desc->local_blocks,
                                      user_mask ? nullptr : score, user_mask, mask, kv_idx, kv_cnt,
                                      (hipStream_t)stream));
+}
+
+bsp_status bsp_score_rescue(const bsp_desc *desc, const void *k, const float *q_pool,
+                            const float *k_pool, float *k_radius, float *rescue, void *stream) {
+  bsp_status st = check_desc(desc, true);
+  if (st != BSP_OK) return st;
+  if (desc->seq == 0) return BSP_OK;
+  if (!k || !q_pool || !k_pool || !k_radius || !rescue) return BSP_ERR_NULL_POINTER;
+  const bool fp8 = desc->dtype == BSP_DTYPE_FP8_E4M3;
+  if (fp8 && !desc->k_scale) return BSP_ERR_BAD_DTYPE;
+  if (!fp8 && (desc->q_scale || desc->k_scale || desc->v_scale)) return BSP_ERR_BAD_DTYPE;
+  const Shape s = shape_of(desc);
+  hipStream_t hs = (hipStream_t)stream;
+  if (bsp::launch_radius(s, k, desc->k_scale, k_pool, k_radius, hs) != hipSuccess)
+    return BSP_ERR_HIP;
+  return hip_status(bsp::launch_score(s, scale_of(desc), q_pool, k_pool, k_radius, rescue, hs));
+}
+
+bsp_status bsp_mask_dual(const bsp_desc *desc, const float *score, const float *rescue,
+                         float gamma_rescue, uint8_t *mask, int32_t *kv_idx, int32_t *kv_cnt,
+                         void *stream) {
+  bsp_status st = check_desc(desc, false);
+  if (st != BSP_OK) return st;
+  if (!(desc->gamma >= 0.f && desc->gamma <= 1.f)) return BSP_ERR_BAD_VALUE;
+  if (!(gamma_rescue >= 0.f && gamma_rescue <= 1.f)) return BSP_ERR_BAD_VALUE;
+  if (desc->sink_blocks < 0 || desc->local_blocks < 0) return BSP_ERR_BAD_VALUE;
+  if (desc->seq == 0) return BSP_OK;
+  if (!score || !rescue || !kv_idx || !kv_cnt) return BSP_ERR_NULL_POINTER;
+  const Shape s = shape_of(desc);
+  return hip_status(bsp::launch_mask(s, desc->gamma, desc->sink_blocks, desc->local_blocks, score,
+                                     nullptr, mask, kv_idx, kv_cnt, (hipStream_t)stream, rescue,
+                                     gamma_rescue));
 }
 
 bsp_status bsp_attn_fwd(const bsp_desc *desc, const void *q, const void *k, const void *v,

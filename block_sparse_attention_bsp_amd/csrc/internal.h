@@ -23,12 +23,17 @@ struct AttnArgs {
 hipError_t launch_pool(const Shape &s, const void *q, const void *k, const float *q_scale,
                        const float *k_scale, float *q_pool, float *k_pool, hipStream_t st);
 hipError_t launch_score(const Shape &s, float c, const float *q_pool, const float *k_pool,
-                        float *score, hipStream_t st);
+                        const float *k_radius, float *score, hipStream_t st);
+hipError_t launch_radius(const Shape &s, const void *k, const float *k_scale, const float *k_pool,
+                         float *k_radius, hipStream_t st);
 hipError_t launch_score_arith(const Shape &s, float c, const void *q, const float *k_pool,
                               float *score, const float *q_scale, hipStream_t st);
+// rescue != nullptr (and no user mask): a block is also kept when its rescue
+// score reaches gamma_r times the row's maximum rescue score.
 hipError_t launch_mask(const Shape &s, float gamma, int sink_blocks, int local_blocks,
                        const float *score, const uint8_t *user_mask, uint8_t *mask,
-                       int32_t *kv_idx, int32_t *kv_cnt, hipStream_t st);
+                       int32_t *kv_idx, int32_t *kv_cnt, hipStream_t st,
+                       const float *rescue = nullptr, float gamma_r = 0.f);
 hipError_t launch_attn_f32(const Shape &s, const AttnArgs &a, hipStream_t st);
 hipError_t launch_attn_bf16(const Shape &s, const AttnArgs &a, hipStream_t st);
 hipError_t launch_attn_fp8(const Shape &s, const AttnArgs &a, hipStream_t st);

@@ -10,17 +10,26 @@
 // max-reduction; the kept set is compacted in ascending order from four
 // 64-wide ballots per step: a lane's slot is the popcount of the kept bits of
 // lower lanes plus its own earlier kept elements.
+//
+// Dual-branch form (rescue branch, thelatestinai page, RBS-Attention
+// abstract: the two branches are thresholded independently and their masks
+// combined): a block is kept when its base score reaches gamma times the
+// row's base maximum, or its rescue score reaches gamma_r times the row's
+// rescue maximum, or it is forced.
 #include "device.h"
 #include "internal.h"
 
 namespace bsp {
 
+template <bool DUAL>
 __global__ __launch_bounds__(256) void mask_kernel(const float *__restrict__ P,
+                                                   const float *__restrict__ Pr,
                                                    const uint8_t *__restrict__ user,
                                                    uint8_t *__restrict__ mask,
                                                    int32_t *__restrict__ kv_idx,
                                                    int32_t *__restrict__ kv_cnt, int rows, int nb,
-                                                   float gamma, int sink, int local) {
+                                                   float gamma, float gamma_r, int sink,
+                                                   int local) {
   const int lane = threadIdx.x & 63;
   const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (row >= rows) return;
@@ -38,17 +47,22 @@ __global__ __launch_bounds__(256) void mask_kernel(const float *__restrict__ P,
     }
   };
 
-  float thr = 0.f;
+  float thr = 0.f, thr_r = 0.f;
   if (!user) {
-    float m = -INFINITY;
+    float m = -INFINITY, mr = -INFINITY;
     for (int J0 = 4 * lane; J0 <= I; J0 += 256) {
-      float x[4];
+      float x[4], y[4];
       load4(P + off, J0, x);
+      if constexpr (DUAL) load4(Pr + off, J0, y);
 #pragma unroll
       for (int e = 0; e < 4; ++e)
-        if (J0 + e <= I) m = fmaxf(m, x[e]);
+        if (J0 + e <= I) {
+          m = fmaxf(m, x[e]);
+          if constexpr (DUAL) mr = fmaxf(mr, y[e]);
+        }
     }
     thr = gamma * wave_max(m);
+    if constexpr (DUAL) thr_r = gamma_r * wave_max(mr);
   }
 
   const uint64_t below = (1ull << lane) - 1ull;
@@ -67,12 +81,13 @@ __global__ __launch_bounds__(256) void mask_kernel(const float *__restrict__ P,
           for (int e = 0; e < 4; ++e) keep[e] = J + e < nb && user[off + J + e] != 0;
         }
       } else {
-        float x[4];
+        float x[4], y[4];
         load4(P + off, J, x);
+        if constexpr (DUAL) load4(Pr + off, J, y);
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int Je = J + e;
-          keep[e] = x[e] >= thr || Je < sink || I - Je < local;
+          keep[e] = x[e] >= thr || (DUAL && y[e] >= thr_r) || Je < sink || I - Je < local;
         }
       }
 #pragma unroll
@@ -110,12 +125,14 @@ __global__ __launch_bounds__(256) void mask_kernel(const float *__restrict__ P,
 // Rows of at most 256 * NS blocks under the max-based threshold: the row of
 // P is read from HBM once, all of a lane's loads in flight together, and kept
 // in registers for the decision and the compaction.
-template <int NS>
+template <int NS, bool DUAL>
 __global__ __launch_bounds__(256) void mask_kernel_reg(const float *__restrict__ P,
+                                                       const float *__restrict__ Pr,
                                                        uint8_t *__restrict__ mask,
                                                        int32_t *__restrict__ kv_idx,
                                                        int32_t *__restrict__ kv_cnt, int rows,
-                                                       int nb, float gamma, int sink, int local) {
+                                                       int nb, float gamma, float gamma_r, int sink,
+                                                       int local) {
   const int lane = threadIdx.x & 63;
   const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (row >= rows) return;
@@ -123,30 +140,37 @@ __global__ __launch_bounds__(256) void mask_kernel_reg(const float *__restrict__
   const size_t off = (size_t)row * nb;
   const bool vec = (nb & 3) == 0;  // rows are 16-byte aligned
 
-  float x[NS][4];
-  float m = -INFINITY;
-#pragma unroll
-  for (int t = 0; t < NS; ++t) {
-    const int J = t * 256 + 4 * lane;
+  auto row4 = [&](const float *src, int J, float (&v4)[4]) {
     if (J <= I) {
       if (vec && J + 3 < nb) {
-        const float4 v = *(const float4 *)(P + off + J);
-        x[t][0] = v.x; x[t][1] = v.y; x[t][2] = v.z; x[t][3] = v.w;
+        const float4 v = *(const float4 *)(src + off + J);
+        v4[0] = v.x; v4[1] = v.y; v4[2] = v.z; v4[3] = v.w;
       } else {
 #pragma unroll
-        for (int e = 0; e < 4; ++e) x[t][e] = J + e < nb ? P[off + J + e] : 0.f;
+        for (int e = 0; e < 4; ++e) v4[e] = J + e < nb ? src[off + J + e] : 0.f;
       }
     } else {
 #pragma unroll
-      for (int e = 0; e < 4; ++e) x[t][e] = 0.f;
+      for (int e = 0; e < 4; ++e) v4[e] = 0.f;
     }
+  };
+  float x[NS][4], y[DUAL ? NS : 1][4];
+  float m = -INFINITY, mr = -INFINITY;
+#pragma unroll
+  for (int t = 0; t < NS; ++t) {
+    row4(P, t * 256 + 4 * lane, x[t]);
+    if constexpr (DUAL) row4(Pr, t * 256 + 4 * lane, y[t]);
   }
 #pragma unroll
   for (int t = 0; t < NS; ++t)
 #pragma unroll
     for (int e = 0; e < 4; ++e)
-      if (t * 256 + 4 * lane + e <= I) m = fmaxf(m, x[t][e]);
+      if (t * 256 + 4 * lane + e <= I) {
+        m = fmaxf(m, x[t][e]);
+        if constexpr (DUAL) mr = fmaxf(mr, y[t][e]);
+      }
   const float thr = gamma * wave_max(m);
+  const float thr_r = DUAL ? gamma_r * wave_max(mr) : 0.f;
 
   const uint64_t below = (1ull << lane) - 1ull;
   int n = 0;
@@ -158,7 +182,8 @@ __global__ __launch_bounds__(256) void mask_kernel_reg(const float *__restrict__
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       const int Je = J + e;
-      keep[e] = Je <= I && (x[t][e] >= thr || Je < sink || I - Je < local);
+      keep[e] = Je <= I && (x[t][e] >= thr || (DUAL && y[DUAL ? t : 0][e] >= thr_r) ||
+                            Je < sink || I - Je < local);
     }
     if (vec && J + 3 < nb) {
       *(uint32_t *)(mask + off + J) = (uint32_t)keep[0] | ((uint32_t)keep[1] << 8) |
@@ -187,27 +212,37 @@ __global__ __launch_bounds__(256) void mask_kernel_reg(const float *__restrict__
   if (lane == 0) kv_cnt[row] = n;
 }
 
-hipError_t launch_mask(const Shape &s, float gamma, int sink, int local, const float *score,
-                       const uint8_t *user, uint8_t *mask, int32_t *idx, int32_t *cnt,
-                       hipStream_t st) {
+template <bool DUAL>
+static hipError_t launch_mask_t(const Shape &s, float gamma, float gamma_r, int sink, int local,
+                                const float *score, const float *rescue, const uint8_t *user,
+                                uint8_t *mask, int32_t *idx, int32_t *cnt, hipStream_t st) {
   const int rows = s.hq * s.nb;
   const dim3 grid((rows + 3) / 4), block(256);
+#define BSP_MASK_REG(NS)                                                                       \
+  hipLaunchKernelGGL((mask_kernel_reg<NS, DUAL>), grid, block, 0, st, score, rescue, mask, idx, \
+                     cnt, rows, s.nb, gamma, gamma_r, sink, local)
   if (!user && s.nb <= 256)
-    hipLaunchKernelGGL(mask_kernel_reg<1>, grid, block, 0, st, score, mask, idx, cnt, rows, s.nb,
-                       gamma, sink, local);
+    BSP_MASK_REG(1);
   else if (!user && s.nb <= 512)
-    hipLaunchKernelGGL(mask_kernel_reg<2>, grid, block, 0, st, score, mask, idx, cnt, rows, s.nb,
-                       gamma, sink, local);
+    BSP_MASK_REG(2);
   else if (!user && s.nb <= 1024)
-    hipLaunchKernelGGL(mask_kernel_reg<4>, grid, block, 0, st, score, mask, idx, cnt, rows, s.nb,
-                       gamma, sink, local);
+    BSP_MASK_REG(4);
   else if (!user && s.nb <= 2048)
-    hipLaunchKernelGGL(mask_kernel_reg<8>, grid, block, 0, st, score, mask, idx, cnt, rows, s.nb,
-                       gamma, sink, local);
+    BSP_MASK_REG(8);
   else
-    hipLaunchKernelGGL(mask_kernel, grid, block, 0, st, score, user, mask, idx, cnt, rows, s.nb,
-                       gamma, sink, local);
+    hipLaunchKernelGGL((mask_kernel<DUAL>), grid, block, 0, st, score, rescue, user, mask, idx,
+                       cnt, rows, s.nb, gamma, gamma_r, sink, local);
+#undef BSP_MASK_REG
   return hipGetLastError();
+}
+
+hipError_t launch_mask(const Shape &s, float gamma, int sink, int local, const float *score,
+                       const uint8_t *user, uint8_t *mask, int32_t *idx, int32_t *cnt,
+                       hipStream_t st, const float *rescue, float gamma_r) {
+  if (rescue && !user)
+    return launch_mask_t<true>(s, gamma, gamma_r, sink, local, score, rescue, nullptr, mask, idx,
+                               cnt, st);
+  return launch_mask_t<false>(s, gamma, 0.f, sink, local, score, nullptr, user, mask, idx, cnt, st);
 }
 
 }  // namespace bsp

@@ -17,6 +17,10 @@
 // their row statistics through LDS.  The grid launches the heaviest row
 // groups of every head first.
 //
+// With a key-block radius r (rescue branch, thelatestinai page, RBS-Attention
+// abstract) the same kernels compute c (Qbar_I . Kbar_J + |Qbar_I| r_J), an
+// upper bound on the block's best per-key logit, and its row softmax.
+//
 // score_kernel_reg (rows of at most 1024 blocks): eight wavefronts with at
 // most four tiles each keep their raw scores in registers, so P is written
 // once, normalised, through an LDS transpose that makes every store cover
@@ -28,9 +32,10 @@
 
 namespace bsp {
 
-template <int D>
+template <int D, bool RESC>
 __global__ __launch_bounds__(256) void score_kernel(const float *__restrict__ q_pool,
                                                     const float *__restrict__ k_pool,
+                                                    const float *__restrict__ k_radius,
                                                     float *__restrict__ P, int hq, int hkv, int nb,
                                                     float c2) {
   constexpr int KS = D / 2;  // k-steps; step ks, lane half h <-> dimension ks + KS*h
@@ -62,6 +67,15 @@ __global__ __launch_bounds__(256) void score_kernel(const float *__restrict__ q_
       qb[i + 3] = row_ok ? t.w : 0.f;
     }
   }
+  // rescue branch: |Qbar_I| (the lane holds half of the dimensions)
+  float qn = 0.f;
+  if constexpr (RESC) {
+    float ss = 0.f;
+#pragma unroll
+    for (int i = 0; i < KS; ++i) ss = fmaf(qb[i], qb[i], ss);
+    qn = sqrtf(ss + __shfl_xor(ss, 32, 64));
+  }
+  const float *rad = RESC ? k_radius + (size_t)g * nb : nullptr;
 
   // S^T tile jt: element r of the lane is key block J0 + (r/4)*8 + half*4 + r%4.
   // The 32 Kbar rows of a tile are one contiguous block: each wave loads it
@@ -142,7 +156,8 @@ __global__ __launch_bounds__(256) void score_kernel(const float *__restrict__ q_
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       const int J = jt * 32 + (r / 4) * 8 + half * 4 + (r % 4);
-      s[r] = (J <= Il && J < nb) ? acc[r] * c2 : -INFINITY;
+      const float add = RESC && J < nb ? qn * rad[J] : 0.f;
+      s[r] = (J <= Il && J < nb) ? (acc[r] + add) * c2 : -INFINITY;
       tmax = fmaxf(tmax, s[r]);
     }
     put_tile(jt, s);
@@ -225,9 +240,10 @@ __global__ __launch_bounds__(256) void score_kernel(const float *__restrict__ q_
 // Rows of at most 1024 key blocks: eight wavefronts split the key-block tiles
 // of the group (at most four each) and keep their raw scores in registers,
 // so P is written once, already normalised, and never read back.
-template <int D>
+template <int D, bool RESC>
 __global__ __launch_bounds__(512) void score_kernel_reg(const float *__restrict__ q_pool,
                                                         const float *__restrict__ k_pool,
+                                                        const float *__restrict__ k_radius,
                                                         float *__restrict__ P, int hq, int hkv,
                                                         int nb, float c2) {
   constexpr int KS = D / 2;   // k-steps; step ks, lane half h <-> dimension ks + KS*h
@@ -260,6 +276,15 @@ __global__ __launch_bounds__(512) void score_kernel_reg(const float *__restrict_
       qb[i + 3] = row_ok ? t.w : 0.f;
     }
   }
+  // rescue branch: |Qbar_I| (the lane holds half of the dimensions)
+  float qn = 0.f;
+  if constexpr (RESC) {
+    float ss = 0.f;
+#pragma unroll
+    for (int i = 0; i < KS; ++i) ss = fmaf(qb[i], qb[i], ss);
+    qn = sqrtf(ss + __shfl_xor(ss, 32, 64));
+  }
+  const float *rad = RESC ? k_radius + (size_t)g * nb : nullptr;
 
   constexpr int TF4 = 32 * D / 4 / 64;  // float4 per lane per tile
   constexpr int RS = D + 4;             // padded LDS row stride (floats)
@@ -312,7 +337,8 @@ __global__ __launch_bounds__(512) void score_kernel_reg(const float *__restrict_
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int J = jt * 32 + (r / 4) * 8 + half * 4 + (r % 4);
-        held[t][r] = (J <= Il && J < nb) ? acc[r] * c2 : -INFINITY;
+        const float add = RESC && J < nb ? qn * rad[J] : 0.f;
+        held[t][r] = (J <= Il && J < nb) ? (acc[r] + add) * c2 : -INFINITY;
         tmax = fmaxf(tmax, held[t][r]);
       }
       const float mn = fmaxf(m, tmax);
@@ -401,24 +427,28 @@ __global__ __launch_bounds__(512) void score_kernel_reg(const float *__restrict_
   }
 }
 
-template <int D>
+template <int D, bool RESC>
 static hipError_t launch_score_t(const Shape &s, float c, const float *qp, const float *kp,
-                                 float *S, hipStream_t st) {
+                                 const float *kr, float *S, hipStream_t st) {
   // heaviest row groups of every head first
   dim3 grid(s.hq, (s.nb + 31) / 32);
   if (s.nb <= 1024)
-    hipLaunchKernelGGL(score_kernel_reg<D>, grid, dim3(512), 0, st, qp, kp, S, s.hq, s.hkv, s.nb,
-                       c * kLog2e);
+    hipLaunchKernelGGL((score_kernel_reg<D, RESC>), grid, dim3(512), 0, st, qp, kp, kr, S, s.hq,
+                       s.hkv, s.nb, c * kLog2e);
   else
-    hipLaunchKernelGGL(score_kernel<D>, grid, dim3(256), 0, st, qp, kp, S, s.hq, s.hkv, s.nb,
-                       c * kLog2e);
+    hipLaunchKernelGGL((score_kernel<D, RESC>), grid, dim3(256), 0, st, qp, kp, kr, S, s.hq,
+                       s.hkv, s.nb, c * kLog2e);
   return hipGetLastError();
 }
 
-hipError_t launch_score(const Shape &s, float c, const float *qp, const float *kp, float *S,
-                        hipStream_t st) {
-  if (s.d == 64) return launch_score_t<64>(s, c, qp, kp, S, st);
-  return launch_score_t<128>(s, c, qp, kp, S, st);
+hipError_t launch_score(const Shape &s, float c, const float *q_pool, const float *k_pool,
+                        const float *k_radius, float *S, hipStream_t st) {
+  if (k_radius) {
+    if (s.d == 64) return launch_score_t<64, true>(s, c, q_pool, k_pool, k_radius, S, st);
+    return launch_score_t<128, true>(s, c, q_pool, k_pool, k_radius, S, st);
+  }
+  if (s.d == 64) return launch_score_t<64, false>(s, c, q_pool, k_pool, nullptr, S, st);
+  return launch_score_t<128, false>(s, c, q_pool, k_pool, nullptr, S, st);
 }
 
 }  // namespace bsp

@@ -44,7 +44,7 @@
 extern "C" {
 #endif
 
-#define BSP_ABI_VERSION 3
+#define BSP_ABI_VERSION 4
 
 typedef enum bsp_status {
   BSP_OK = 0,
@@ -150,6 +150,42 @@ bsp_status bsp_score_arith(const bsp_desc *desc, const void *q, const void *k, f
  */
 bsp_status bsp_mask(const bsp_desc *desc, const float *score, const uint8_t *user_mask,
                     uint8_t *mask, int32_t *kv_idx, int32_t *kv_cnt, void *stream);
+
+/*
+ * bsp_score_rescue - rescue branch of the scores (thelatestinai page,
+ * RBS-Attention abstract: a block centroid can hide one highly relevant key;
+ * a rescue branch built on the maximum key-block radius flags such blocks).
+ * The page gives no formula; this library computes
+ *   k_radius[g][J] = max over the valid keys k of block J of ||k - Kbar[g][J]||
+ *   R[h][I][J]     = c * (Qbar[h][I] . Kbar[g][J] + ||Qbar[h][I]|| * k_radius[g][J])
+ * (an upper bound on c * Qbar . k for every key k of the block, by
+ * Cauchy-Schwarz) and, like bsp_score, its softmax over J <= I:
+ *   rescue[h][I][J] = exp(R - max_J' R) / sum_{J' <= I} exp(R - max_J' R), 0 for J > I.
+ *
+ * k:        device, storage dtype, [hkv][seq][d] (re-read for the radii)
+ * q_pool, k_pool: device float, as written by bsp_score on the same inputs
+ * k_radius: device float [hkv][nb]      (written)
+ * rescue:   device float [hq][nb][nb]   (written, every entry)
+ * Needs desc->k_scale for fp8 (q_scale and v_scale are not read).
+ */
+bsp_status bsp_score_rescue(const bsp_desc *desc, const void *k, const float *q_pool,
+                            const float *k_pool, float *k_radius, float *rescue, void *stream);
+
+/*
+ * bsp_mask_dual - the two branches thresholded independently and their masks
+ * combined (RBS-Attention abstract).  For J <= I:
+ *   keep = score[h][I][J]  >= desc->gamma  * max_J'<=I score[h][I][J']
+ *       OR rescue[h][I][J] >= gamma_rescue * max_J'<=I rescue[h][I][J']
+ *       OR J < sink_blocks OR I - J < local_blocks
+ * and 0 for J > I.  Outputs and their layout as for bsp_mask.
+ *
+ * score:   device float [hq][nb][nb] from bsp_score (or bsp_score_arith)
+ * rescue:  device float [hq][nb][nb] from bsp_score_rescue
+ * gamma_rescue: 0 <= gamma_rescue <= 1
+ */
+bsp_status bsp_mask_dual(const bsp_desc *desc, const float *score, const float *rescue,
+                         float gamma_rescue, uint8_t *mask, int32_t *kv_idx, int32_t *kv_cnt,
+                         void *stream);
 
 /*
  * bsp_attn_fwd - stage 3, block-sparse attention (Appendix B "Block Sparse

@@ -28,7 +28,8 @@ def built():
 
 def test_header_declares_the_entry_points():
     assert _declared() == ["bsp_abi_version", "bsp_attn_fwd", "bsp_calibrate_gamma", "bsp_mask",
-                           "bsp_score", "bsp_score_arith", "bsp_status_string"]
+                           "bsp_mask_dual", "bsp_score", "bsp_score_arith", "bsp_score_rescue",
+                           "bsp_status_string"]
 
 
 def test_library_exports_every_declared_symbol():
@@ -141,3 +142,17 @@ def test_calibrate_gamma_host_checks():
     assert bsp.bsp_calibrate_gamma(d0, None, 0.5, 1e-4, None, None, None, None, g, dens,
                                    None) == 0
     assert g.value == 1.0 and dens.value == 1.0
+
+
+def test_rescue_entry_points_host_checks():
+    import ctypes as C
+    fake = C.c_void_p(0x1000)  # never dereferenced: every case fails before a launch
+    d = bsp.desc(4, 1, 1024, 64, 64, bsp.DTYPE_BF16)
+    assert bsp.bsp_score_rescue(d, fake, fake, fake, fake, None, None) == 1
+    d8 = bsp.desc(4, 1, 1024, 64, 64, bsp.DTYPE_FP8_E4M3)
+    assert bsp.bsp_score_rescue(d8, fake, fake, fake, fake, fake, None) == 3  # needs k_scale
+    for gr in (-0.1, 1.1, float("nan")):
+        assert bsp.bsp_mask_dual(d, fake, fake, gr, fake, fake, fake, None) == 4
+    assert bsp.bsp_mask_dual(d, fake, None, 0.5, fake, fake, fake, None) == 1
+    d0 = bsp.desc(4, 1, 0, 64, 64, bsp.DTYPE_BF16)
+    assert bsp.bsp_score_rescue(d0, None, None, None, None, None, None) == 0

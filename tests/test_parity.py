@@ -164,6 +164,76 @@ def test_score_arith_matches_oracle(which):
     print(f"  density {dens:.3f} band blocks {nband}", flush=True)
 
 
+def _check_dual(gm, gidx, gcnt, P, Pr, g, gr, om, ocnt):
+    """Dual mask equal to the oracle's outside either branch's band."""
+    b = H.band(P, g, 1, 1) | H.band(Pr, gr, 1, 1)
+    diff = gm != om
+    assert not np.any(diff & ~b), f"{int((diff & ~b).sum())} blocks differ outside the bands"
+    want_idx, want_cnt = H.idx_from_mask(gm)
+    assert np.array_equal(gcnt, want_cnt)
+    keep = np.arange(gm.shape[-1])[None, None, :] < want_cnt[..., None]
+    assert np.array_equal(np.where(keep, gidx, -1), want_idx)
+    clean = ~b.any(-1)
+    assert np.array_equal(gcnt[clean], ocnt[clean])
+    return int(b.sum())
+
+
+@pytest.mark.parametrize("which", ["s1_0", "s1_2", "bf16_128_128_1000", "bf16_64_64_777",
+                                   "fp8_128_128_1000", "fp8_64_64_700", "f32_128_64_333",
+                                   "llama_4k", "qwen_4k_fp8"])
+def test_rescue_branch_matches_oracle(which):
+    """Key-block radii, rescue scores and the dual-branch mask."""
+    announce(f"rescue branch {which}")
+    c = _arith_case(which)
+    d = H.dev(c)
+    qp, kp, sc = bsp.score(d["q"], d["k"], c.block, q_scale=d["q_scale"], k_scale=d["k_scale"])
+    kr, rs = bsp.score_rescue(d["k"], qp, kp, c.seq, c.block, k_scale=d["k_scale"])
+    g, gr = c.gamma, 0.5
+    m, idx, cnt = bsp.mask_dual(sc, rs, g, gr, c.seq, c.block)
+    torch.cuda.synchronize()
+    cs = 1.0 / math.sqrt(c.d)
+    qb = oracle.pool(c.q, c.dtype, c.block, c.q_scale)
+    kb = oracle.pool(c.k, c.dtype, c.block, c.k_scale)
+    _, P = oracle.score(qb, kb, cs)
+    r = oracle.key_radius(c.k, c.dtype, c.block, c.k_scale)
+    _, Pr = oracle.score_rescue(qb, kb, r, cs)
+    np.testing.assert_allclose(kr.cpu().numpy(), r, rtol=1e-5, atol=1e-5)
+    np.testing.assert_allclose(rs.cpu().numpy(), Pr, rtol=1e-4, atol=1e-6)
+    om, oidx, ocnt = oracle.mask_dual(P, Pr, g, gr)
+    nband = _check_dual(m.cpu().numpy(), idx.cpu().numpy(), cnt.cpu().numpy(), P, Pr, g, gr, om,
+                        ocnt)
+    base = oracle.mask(P, g)[0].sum()
+    print(f"  kept {om.sum()} (base alone {base}), band blocks {nband}", flush=True)
+
+
+def test_long_rows_over_2048_blocks():
+    """nb = 2188: the general score kernel and the general mask path, base and
+    rescue branches, against the oracle."""
+    announce("long rows nb=2188")
+    c = gen.make_case(2, 1, 2188 * 64, 64, 64, "bf16", 21, gamma=0.2, rope=True, n_vert=8,
+                      slash=True, block_offset=1.0)
+    d = H.dev(c)
+    qp, kp, sc = bsp.score(d["q"], d["k"], c.block)
+    m, idx, cnt = bsp.mask(sc, c.gamma, c.seq, c.block)
+    kr, rs = bsp.score_rescue(d["k"], qp, kp, c.seq, c.block)
+    md, idxd, cntd = bsp.mask_dual(sc, rs, c.gamma, 0.5, c.seq, c.block)
+    torch.cuda.synchronize()
+    cs = 1.0 / math.sqrt(c.d)
+    qb = oracle.pool(c.q, c.dtype, c.block)
+    kb = oracle.pool(c.k, c.dtype, c.block)
+    _, P = oracle.score(qb, kb, cs)
+    np.testing.assert_allclose(sc.cpu().numpy(), P, rtol=1e-4, atol=1e-6)
+    om, oidx, ocnt = oracle.mask(P, c.gamma)
+    H.check_mask(m.cpu().numpy(), idx.cpu().numpy(), cnt.cpu().numpy(),
+                 dict(P=P, mask=om, idx=oidx, cnt=ocnt), c.gamma)
+    r = oracle.key_radius(c.k, c.dtype, c.block)
+    _, Pr = oracle.score_rescue(qb, kb, r, cs)
+    np.testing.assert_allclose(rs.cpu().numpy(), Pr, rtol=1e-4, atol=1e-6)
+    omd, _, ocntd = oracle.mask_dual(P, Pr, c.gamma, 0.5)
+    _check_dual(md.cpu().numpy(), idxd.cpu().numpy(), cntd.cpu().numpy(), P, Pr, c.gamma, 0.5,
+                omd, ocntd)
+
+
 @pytest.mark.parametrize("which,target", [("s1_0", 0.3), ("s1_1", 0.7), ("llama_4k", 0.7)])
 def test_calibrate_gamma_matches_oracle(which, target):
     """Bisection on the GPU masks lands on the oracle's gamma; the buffers
