@@ -60,6 +60,10 @@ def parse():
     p.add_argument("--rescue", type=float, default=None, metavar="GAMMA_R",
                    help="add the radius-based rescue branch (bsp_score_rescue + bsp_mask_dual) "
                         "with this threshold factor")
+    p.add_argument("--varlen", action="store_true",
+                   help="time bsp_attn_fwd_varlen instead: a packed batch of the config's heads "
+                        "with seeded lengths (log-uniform 1K-32K tokens, 128K in all) over a "
+                        "shuffled paged cache, dense causal per sequence")
     p.add_argument("--calibrate", type=float, default=None, metavar="TARGET",
                    help="also time bsp_calibrate_gamma for this target density")
     p.add_argument("--copy-calibration", action="store_true",
@@ -136,6 +140,69 @@ def cpu_baseline(case, gpu_mask, nrows):
     }
 
 
+def varlen_main(a):
+    """Paged variable-length attention on one packed batch (attention stage
+    only; each sequence dense causal)."""
+    import torch
+    import block_sparse_attention_bsp_amd as bsp
+    import gen
+    torch.cuda.set_device(0)
+    cfg = gen.CONFIGS[a.config]
+    hq, hkv, d, B = cfg["hq"], cfg["hkv"], cfg["d"], cfg["block"]
+    rng = np.random.default_rng(2024)
+    lens, total = [], 131072
+    while sum(lens) < total:
+        n = int(np.exp(rng.uniform(np.log(1024), np.log(32768))))
+        lens.append(min(n, total - sum(lens)))
+    nbs = [-(-n // B) for n in lens]
+    tb, ntok = sum(nbs), sum(lens)
+    dt = torch.bfloat16 if cfg["dtype"] == "bf16" else torch.float8_e4m3fn
+    g = torch.Generator(device="cuda").manual_seed(7)
+    q = torch.randn((hq, ntok, d), device="cuda", generator=g).to(dt)
+    kc = torch.randn((tb, hkv, B, d), device="cuda", generator=g).to(dt)
+    vc = torch.randn((tb, hkv, B, d), device="cuda", generator=g).to(dt)
+    perm = torch.from_numpy(rng.permutation(tb).astype(np.int32))
+    ptab = torch.zeros((len(lens), max(nbs)), dtype=torch.int32)
+    b0 = 0
+    for s, nb in enumerate(nbs):
+        ptab[s, :nb] = perm[b0:b0 + nb]
+        b0 += nb
+    ptab = ptab.cuda()
+    sc = {}
+    if cfg["dtype"] == "fp8":
+        sc = {k: torch.ones(n, device="cuda") for k, n in
+              (("q_scale", hq), ("k_scale", hkv), ("v_scale", hkv))}
+    run = lambda: bsp.attn_fwd_varlen(q, kc, vc, ptab, lens, B, **sc)
+    for _ in range(a.warmup):
+        run()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    e0.record()
+    for _ in range(a.steps):
+        run()
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / a.steps
+    wall = (time.perf_counter() - t0) * 1e3 / a.steps
+    F = sum(dense_flops(hq, n, d) for n in lens)
+    peak = PEAK_FP8_TFLOPS if cfg["dtype"] == "fp8" else PEAK_BF16_TFLOPS
+    tf = F / (ms * 1e-3) / 1e12
+    print(json.dumps({
+        "metric": "paged varlen prefill-attn TFLOP/s (dense causal per sequence)",
+        "value": round(tf, 3), "unit": "TFLOP/s", "n_gpus": 1, "steps": a.steps,
+        "warmup": a.warmup, "ms_per_step": round(wall, 4), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": cfg["dtype"],
+        "data": "synthetic (random N(0,1) q and paged K/V, seeded length mix)",
+        "config": {"workload": f"{len(lens)} sequences, {ntok} tokens, {hq} q / {hkv} kv heads, "
+                               f"d {d}, block {B}, pages shuffled", "lengths": lens},
+        "attn_ms": round(ms, 4),
+        "roofline": {"bound": "mfma", "achieved": round(tf, 3), "peak": peak,
+                     "unit": "TFLOP/s", "frac": round(tf / peak, 4), "traffic": None,
+                     "kernel": "attn_mfma_kernel (varlen)", "flops_per_launch": F},
+    }), flush=True)
+
+
 def main():
     a = parse()
     if a.gpus != 1:
@@ -152,6 +219,8 @@ def main():
         build.build()
     assert torch.cuda.is_available(), "needs a GPU"
     torch.cuda.set_device(0)
+    if a.varlen:
+        return varlen_main(a)
 
     c = gen.make_s2(a.config, seq=a.seq) if a.s2 else gen.make_config(a.config, seq=a.seq)
     hq, hkv, seq, d, B = c.hq, c.hkv, c.seq, c.d, c.block

@@ -13,6 +13,7 @@ index compaction) and ``attn_fwd`` (block-sparse online-softmax attention);
 from __future__ import annotations
 
 import ctypes
+import itertools
 import os
 from typing import Optional
 
@@ -22,6 +23,7 @@ __all__ = [
     "BspError", "BspDesc", "lib", "library_path", "desc", "score", "mask", "attn_fwd", "prefill",
     "calibrate_gamma", "score_arith", "score_rescue", "mask_dual", "bsp_score", "bsp_score_arith",
     "bsp_score_rescue", "bsp_mask", "bsp_mask_dual", "bsp_attn_fwd", "bsp_calibrate_gamma",
+    "BspVarlen", "bsp_attn_fwd_varlen", "attn_fwd_varlen",
     "bsp_status_string", "bsp_abi_version",
     "DTYPE_F32", "DTYPE_BF16", "DTYPE_FP8_E4M3",
 ]
@@ -43,6 +45,16 @@ class BspDesc(ctypes.Structure):
         ("sink_blocks", ctypes.c_int32), ("local_blocks", ctypes.c_int32),
         ("dtype", ctypes.c_int32), ("q_scale", ctypes.c_void_p), ("k_scale", ctypes.c_void_p),
         ("v_scale", ctypes.c_void_p),
+    ]
+
+
+class BspVarlen(ctypes.Structure):
+    """Mirror of ``bsp_varlen`` in include/bsp.h."""
+    _fields_ = [
+        ("cu_seqlens", ctypes.c_void_p), ("cu_blocks", ctypes.c_void_p),
+        ("page_table", ctypes.c_void_p), ("nseq", ctypes.c_int32),
+        ("total_blocks", ctypes.c_int32), ("max_pages", ctypes.c_int32),
+        ("idx_stride", ctypes.c_int32), ("block_order", ctypes.c_void_p),
     ]
 
 
@@ -70,11 +82,14 @@ def lib():
         L.bsp_score_rescue.argtypes = [P, vp, vp, vp, vp, vp, vp]
         L.bsp_mask_dual.argtypes = [P, vp, vp, ctypes.c_float, vp, vp, vp, vp]
         L.bsp_attn_fwd.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp]
+        L.bsp_attn_fwd_varlen.argtypes = [P, ctypes.POINTER(BspVarlen), vp, vp, vp, vp, vp, vp,
+                                          vp, vp]
         f32 = ctypes.c_float
         L.bsp_calibrate_gamma.argtypes = [P, vp, f32, f32, vp, vp, vp, vp,
                                           ctypes.POINTER(f32), ctypes.POINTER(f32), vp]
         for f in (L.bsp_score, L.bsp_score_arith, L.bsp_score_rescue, L.bsp_mask,
-                  L.bsp_mask_dual, L.bsp_attn_fwd, L.bsp_calibrate_gamma):
+                  L.bsp_mask_dual, L.bsp_attn_fwd, L.bsp_attn_fwd_varlen,
+                  L.bsp_calibrate_gamma):
             f.restype = ctypes.c_int32
         L.bsp_status_string.argtypes = [ctypes.c_int32]
         L.bsp_status_string.restype = ctypes.c_char_p
@@ -128,6 +143,12 @@ def bsp_calibrate_gamma(d: BspDesc, score_in, target: float, tol: float, mask_ou
     return lib().bsp_calibrate_gamma(ctypes.byref(d), score_in, target, tol, mask_out, kv_idx,
                                      kv_cnt, cnt_host, ctypes.byref(gamma_out),
                                      ctypes.byref(density_out), stream)
+
+
+def bsp_attn_fwd_varlen(d: BspDesc, vl: BspVarlen, q, k_cache, v_cache, kv_idx, kv_cnt, o, lse,
+                        stream) -> int:
+    return lib().bsp_attn_fwd_varlen(ctypes.byref(d), ctypes.byref(vl), q, k_cache, v_cache,
+                                     kv_idx, kv_cnt, o, lse, stream)
 
 
 # ---------------------------------------------------------------- torch level
@@ -321,6 +342,63 @@ def attn_fwd(q, k, v, block: int, kv_idx=None, kv_cnt=None, sm_scale: float = 0.
     _shape(lse, (hq, seq), "lse")
     _check(bsp_attn_fwd(dsc, _ptr(q), _ptr(k), _ptr(v), _ptr(kv_idx), _ptr(kv_cnt), _ptr(o),
                         _ptr(lse), _stream()))
+    return o, lse
+
+
+def attn_fwd_varlen(q, k_cache, v_cache, page_table, seqlens, block: int, kv_idx=None,
+                    kv_cnt=None, sm_scale: float = 0.0, q_scale=None, k_scale=None,
+                    v_scale=None, want_lse: bool = True, block_order=None):
+    """Packed variable-length batch over a paged cache (bsp_attn_fwd_varlen).
+    q: [hq, sum(seqlens), d]; k_cache, v_cache: [pages, hkv, block, d];
+    page_table: int32 [nseq, max_pages]; seqlens: host list of lengths;
+    kv_idx: int32 [hq, total_blocks, stride] with kv_cnt [hq, total_blocks];
+    block_order: optional int32 [total_blocks] launch order of the blocks.
+    Returns (o, lse) over the packed tokens."""
+    lens = [int(x) for x in seqlens]
+    if not lens or min(lens) < 0:
+        raise BspError(2, "seqlens must be a non-empty list of lengths >= 0")
+    hq, ntok, d = q.shape
+    if ntok != sum(lens):
+        raise BspError(2, "q's token axis must equal sum(seqlens)")
+    if k_cache.dim() != 4 or k_cache.shape[2] != block or k_cache.shape[3] != d:
+        raise BspError(2, "k_cache must be [pages, hkv, block, d]")
+    _shape(v_cache, k_cache.shape, "v_cache")
+    hkv = k_cache.shape[1]
+    for t in (k_cache, v_cache):
+        if t.dtype != q.dtype:
+            raise BspError(3, "q and the caches must share one dtype")
+    nbs = [-(-n // block) for n in lens]
+    nseq = len(lens)
+    if page_table.dim() != 2 or page_table.shape[0] != nseq or page_table.dtype != torch.int32:
+        raise BspError(2, "page_table must be int32 [nseq, max_pages]")
+    if page_table.shape[1] < max(nbs + [1]):
+        raise BspError(2, "page_table rows are shorter than a sequence's block count")
+    tb = sum(nbs)
+    cu_s = torch.tensor([0] + list(itertools.accumulate(lens)), dtype=torch.int32, device=q.device)
+    cu_b = torch.tensor([0] + list(itertools.accumulate(nbs)), dtype=torch.int32, device=q.device)
+    stride = 1
+    if kv_idx is not None:
+        if kv_idx.dim() != 3 or kv_idx.shape[:2] != (hq, tb) or kv_idx.dtype != torch.int32:
+            raise BspError(2, "kv_idx must be int32 [hq, total_blocks, stride]")
+        stride = kv_idx.shape[2]
+        _shape(kv_cnt, (hq, tb), "kv_cnt")
+        if kv_cnt.dtype != torch.int32:
+            raise BspError(3, "kv_cnt must be int32")
+    for name, t, want in (("q_scale", q_scale, hq), ("k_scale", k_scale, hkv),
+                          ("v_scale", v_scale, hkv)):
+        _shape(t, (want,), name)
+    dsc = desc(hq, hkv, ntok, d, block, _dtype_code(q), sm_scale=sm_scale, q_scale=q_scale,
+               k_scale=k_scale, v_scale=v_scale)
+    if block_order is not None:
+        _shape(block_order, (tb,), "block_order")
+        if block_order.dtype != torch.int32:
+            raise BspError(3, "block_order must be int32")
+    vl = BspVarlen(_ptr(cu_s), _ptr(cu_b), _ptr(page_table), nseq, tb, page_table.shape[1], stride,
+                   _ptr(block_order))
+    o = torch.empty((hq, ntok, d), dtype=torch.bfloat16, device=q.device)
+    lse = torch.empty((hq, ntok), dtype=torch.float32, device=q.device) if want_lse else None
+    _check(bsp_attn_fwd_varlen(dsc, vl, _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(kv_idx),
+                               _ptr(kv_cnt), _ptr(o), _ptr(lse), _stream()))
     return o, lse
 
 

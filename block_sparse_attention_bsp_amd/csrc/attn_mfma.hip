@@ -173,30 +173,34 @@ struct Attn {
     }
   }
 
-  // Sub-tile (J, sub) -> LDS buffers, issued one sub-tile ahead.  K (and bf16
-  // V) go straight to LDS; fp8 V comes back in registers for widening.
-  __device__ __forceinline__ void issue(int J, int sub, uint8_t *Kb, uint16_t *Vb) {
-    const int j0 = J * BLK + sub * KT;
-    const uint32_t ksoff = (uint32_t)j0 * RB, vsoff = (uint32_t)j0 * (D * 2);
-    if (j0 + KT <= seq) {
+  // Rows [r0, r0 + KT) of a K/V region -> LDS buffers, issued one sub-tile
+  // ahead.  kr / vr describe the region (one kv head's sequence, or one cache
+  // page), vb is its V base for fp8, lim the number of valid rows in it.  K
+  // (and bf16 V) go straight to LDS; fp8 V comes back in registers for
+  // widening.
+  __device__ __forceinline__ void issue_rows(__amdgpu_buffer_rsrc_t kr, __amdgpu_buffer_rsrc_t vr,
+                                             const uint8_t *vb, int r0, int lim, uint8_t *Kb,
+                                             uint16_t *Vb) {
+    const uint32_t ksoff = (uint32_t)r0 * RB, vsoff = (uint32_t)r0 * (D * 2);
+    if (r0 + KT <= lim) {
 #pragma unroll
-      for (int it = 0; it < KPW / 64; ++it) lds_dma16(krs, kdma[it], ksoff, Kb + (w * KPW + it * 64) * 16);
+      for (int it = 0; it < KPW / 64; ++it) lds_dma16(kr, kdma[it], ksoff, Kb + (w * KPW + it * 64) * 16);
       if constexpr (DT == kBF16) {
 #pragma unroll
         for (int it = 0; it < VPW / 64; ++it)
-          lds_dma16(vrs, vdma[it], vsoff, (uint8_t *)Vb + (w * VPW + it * 64) * 16);
+          lds_dma16(vr, vdma[it], vsoff, (uint8_t *)Vb + (w * VPW + it * 64) * 16);
       }
     } else {
-      // ragged last block: rows past the end re-read the last row (finite data
-      // whose keys are masked as causal-future for every valid query)
+      // ragged last block: rows past the end re-read the last valid row
+      // (finite data whose keys are masked as causal-future for every query)
 #pragma unroll
       for (int it = 0; it < KPW / 64; ++it)
-        lds_dma16(krs, kdma[it] - (uint32_t)max(0, j0 + krow[it] - (seq - 1)) * RB, ksoff,
+        lds_dma16(kr, kdma[it] - (uint32_t)max(0, r0 + krow[it] - (lim - 1)) * RB, ksoff,
                   Kb + (w * KPW + it * 64) * 16);
       if constexpr (DT == kBF16) {
 #pragma unroll
         for (int it = 0; it < VPW / 64; ++it)
-          lds_dma16(vrs, vdma[it] - (uint32_t)max(0, j0 + vrow[it] - (seq - 1)) * (D * 2), vsoff,
+          lds_dma16(vr, vdma[it] - (uint32_t)max(0, r0 + vrow[it] - (lim - 1)) * (D * 2), vsoff,
                     (uint8_t *)Vb + (w * VPW + it * 64) * 16);
       }
     }
@@ -205,10 +209,15 @@ struct Attn {
       for (int it = 0; it < VPER; ++it) {
         const int e = threadIdx.x + it * NT;
         const int r = e / (RB / 16), c = e % (RB / 16);
-        const int jr = min(j0 + r, seq - 1);
-        vreg[it] = *(const uint4 *)(v + (kvrow0 + jr) * RB + c * 16);
+        const int jr = min(r0 + r, lim - 1);
+        vreg[it] = *(const uint4 *)(vb + (size_t)jr * RB + c * 16);
       }
     }
+  }
+
+  // Sub-tile (J, sub) of this kv head's contiguous K/V
+  __device__ __forceinline__ void issue(int J, int sub, uint8_t *Kb, uint16_t *Vb) {
+    issue_rows(krs, vrs, v + kvrow0 * RB, J * BLK + sub * KT, seq, Kb, Vb);
   }
 
   // fp8 only: widen the prefetched V codes to bf16 into the LDS buffer.
@@ -368,13 +377,22 @@ struct Attn {
   }
 };
 
-template <int DT, int D, int BLK>
+// Packed variable-length batch over a paged K/V cache (VL): sequence s owns
+// tokens cu_seqlens[s] .. cu_seqlens[s+1] of q / o / lse and query blocks
+// cu_blocks[s] .. cu_blocks[s+1] of the grid; key block J of sequence s is
+// cache page page_table[s * max_pages + J], laid out [page][hkv][BLK][d].
+struct VarlenDev {
+  const int32_t *cu_seqlens, *cu_blocks, *page_table, *block_order;
+  int nseq, max_pages, idx_stride;
+};
+
+template <int DT, int D, int BLK, bool VL>
 __global__ __launch_bounds__(BLK * 2, 256 / BLK) void attn_mfma_kernel(
     const uint8_t *__restrict__ q, const uint8_t *__restrict__ k, const uint8_t *__restrict__ v,
     const int32_t *__restrict__ kv_idx, const int32_t *__restrict__ kv_cnt,
     uint16_t *__restrict__ o, float *__restrict__ lse, const float *__restrict__ q_scale,
     const float *__restrict__ k_scale, const float *__restrict__ v_scale, int hq, int hkv,
-    int seq, int nb, float sm_scale_log2, int xcd_map) {
+    int seq, int nb, float sm_scale_log2, int xcd_map, VarlenDev vl) {
   using A = Attn<DT, D, BLK>;
   using C = typename A::C;
   constexpr int RB = C::RB, LB = C::LB, DK = C::DK, KT = C::KT, NSUB = C::NSUB;
@@ -406,16 +424,49 @@ __global__ __launch_bounds__(BLK * 2, 256 / BLK) void attn_mfma_kernel(
     }
   }
   const int g = h / grp;
+  // token rows of q / o / lse: ntok per head, this sequence from tok0; len
+  // tokens in this sequence; the kv list row and its stride
+  const int ntok = seq;
+  int len = seq, tok0 = 0, gb = I, stride = nb;
+  const int32_t *ptab = nullptr;
+  if constexpr (VL) {
+    // launch order: the caller's permutation (heaviest first), if given
+    if (vl.block_order) gb = vl.block_order[nb - 1 - I];
+    int lo = 0, hi = vl.nseq;  // the sequence whose blocks contain gb
+    while (hi - lo > 1) {
+      const int mid = (lo + hi) >> 1;
+      if (vl.cu_blocks[mid] <= gb) lo = mid; else hi = mid;
+    }
+    I = gb - vl.cu_blocks[lo];
+    tok0 = vl.cu_seqlens[lo];
+    len = vl.cu_seqlens[lo + 1] - tok0;
+    ptab = vl.page_table + (size_t)lo * vl.max_pages;
+    stride = vl.idx_stride;
+  }
   T.I = I;
-  T.seq = seq;
+  T.seq = len;
   T.k = k;
   T.v = v;
   T.kvrow0 = (size_t)g * seq;
-  T.krs = make_rsrc(k + T.kvrow0 * RB, (uint32_t)seq * RB);
-  T.vrs = make_rsrc(v + T.kvrow0 * (DT == kBF16 ? D * 2 : RB), (uint32_t)seq * (DT == kBF16 ? D * 2 : RB));
+  if constexpr (!VL) {
+    T.krs = make_rsrc(k + T.kvrow0 * RB, (uint32_t)seq * RB);
+    T.vrs = make_rsrc(v + T.kvrow0 * (DT == kBF16 ? D * 2 : RB),
+                      (uint32_t)seq * (DT == kBF16 ? D * 2 : RB));
+  }
+  // key block J -> LDS, through the page table for VL
+  constexpr int VRB = DT == kBF16 ? D * 2 : RB;  // bytes per V row in memory
+  auto issue_block = [&](int J, int sub, uint8_t *Kb, uint16_t *Vb) {
+    if constexpr (VL) {
+      const size_t slab = ((size_t)ptab[J] * hkv + g) * BLK;
+      T.issue_rows(make_rsrc(k + slab * RB, BLK * RB), make_rsrc(v + slab * VRB, BLK * VRB),
+                   v + slab * VRB, sub * KT, min(BLK, len - J * BLK), Kb, Vb);
+    } else {
+      T.issue(J, sub, Kb, Vb);
+    }
+  };
   T.qi[0] = I * BLK + T.w * 32 + T.r16;
   T.qi[1] = T.qi[0] + 16;
-  const size_t row = (size_t)h * nb + I;
+  const size_t row = (size_t)h * nb + gb;  // kv list row (gb == I unless VL)
   T.scale2 = sm_scale_log2;
   if constexpr (DT == kFP8) T.scale2 *= q_scale[h] * k_scale[g];
   T.setup();
@@ -427,11 +478,11 @@ __global__ __launch_bounds__(BLK * 2, 256 / BLK) void attn_mfma_kernel(
     const int qq = T.qi[qt];
 #pragma unroll
     for (int ks = 0; ks < DK; ++ks) {
-      const uint8_t *src = q + ((size_t)h * seq + min(qq, seq - 1)) * RB +
+      const uint8_t *src = q + ((size_t)h * ntok + tok0 + min(qq, len - 1)) * RB +
                            (DT == kFP8 ? T.g * LB : (ks * 32 + 8 * T.g) * 2);
       uint4 a = *(const uint4 *)src, b = make_uint4(0, 0, 0, 0);
       if constexpr (LB == 32) b = *(const uint4 *)(src + 16);
-      if (qq >= seq) a = b = make_uint4(0, 0, 0, 0);
+      if (qq >= len) a = b = make_uint4(0, 0, 0, 0);
       if constexpr (DT == kFP8) {
         const uint4 ab[2] = {a, b};
         __builtin_memcpy(&T.qf[qt][ks], ab, 32);
@@ -445,8 +496,8 @@ __global__ __launch_bounds__(BLK * 2, 256 / BLK) void attn_mfma_kernel(
   T.m_used[0] = T.m_used[1] = -INFINITY;
   T.l[0] = T.l[1] = 0.f;
 
-  const int nblk = kv_idx ? max(0, min(kv_cnt[row], nb)) : I + 1;
-  const int32_t *ilist = kv_idx ? kv_idx + row * nb : nullptr;
+  const int nblk = kv_idx ? max(0, min(kv_cnt[row], stride)) : I + 1;
+  const int32_t *ilist = kv_idx ? kv_idx + row * stride : nullptr;
   const int ns = nblk * NSUB;
   // The kv list streams through registers 64 entries at a time: lane l holds
   // entry 64c + l of chunk c, and chunk c + 1 is loaded on entering chunk c.
@@ -474,7 +525,7 @@ __global__ __launch_bounds__(BLK * 2, 256 / BLK) void attn_mfma_kernel(
   // barrier, issues sub-tile i+1 into the other buffer and computes i.
   int Jc = ns > 0 ? block_of(0) : -1;
   if (Jc >= 0) {
-    T.issue(Jc, 0, Ks0, Vs0);
+    issue_block(Jc, 0, Ks0, Vs0);
     if constexpr (DT == kFP8) T.store_v(Vs0);
   }
   for (int i = 0; i < ns; i += 2) {
@@ -485,7 +536,7 @@ __global__ __launch_bounds__(BLK * 2, 256 / BLK) void attn_mfma_kernel(
         const int Jn = ii + 1 < ns ? block_of((ii + 1) / NSUB) : -1;
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         __syncthreads();
-        if (Jn >= 0) T.issue(Jn, (ii + 1) % NSUB, ph ? Ks0 : Ks1, ph ? Vs0 : Vs1);
+        if (Jn >= 0) issue_block(Jn, (ii + 1) % NSUB, ph ? Ks0 : Ks1, ph ? Vs0 : Vs1);
         if (Jc >= 0)
           T.compute(ph ? Ks1 : Ks0, ph ? Vs1 : Vs0, Jc * BLK + (ii % NSUB) * KT, Jc == I);
         if constexpr (DT == kFP8) {
@@ -503,10 +554,10 @@ __global__ __launch_bounds__(BLK * 2, 256 / BLK) void attn_mfma_kernel(
     lt += __shfl_xor(lt, 16, 64);
     lt += __shfl_xor(lt, 32, 64);
     const int qq = T.qi[qt];
-    if (qq < seq) {
+    if (qq < len) {
       float inv = lt > 0.f ? 1.f / lt : 0.f;
       if constexpr (DT == kFP8) inv *= v_scale[g];
-      uint16_t *orow = o + ((size_t)h * seq + qq) * D;
+      uint16_t *orow = o + ((size_t)h * ntok + tok0 + qq) * D;
 #pragma unroll
       for (int dt = 0; dt < C::NDT; ++dt) {
         uint2 pk;
@@ -517,7 +568,7 @@ __global__ __launch_bounds__(BLK * 2, 256 / BLK) void attn_mfma_kernel(
         *(uint2 *)(orow + dt * 16 + 4 * T.g) = pk;
       }
       if (lse && T.g == 0)
-        lse[(size_t)h * seq + qq] = lt > 0.f ? (T.m_used[qt] + log2f(lt)) * kLn2 : -INFINITY;
+        lse[(size_t)h * ntok + tok0 + qq] = lt > 0.f ? (T.m_used[qt] + log2f(lt)) * kLn2 : -INFINITY;
     }
   }
 }
@@ -526,10 +577,25 @@ template <int DT, int D, int BLK>
 static hipError_t launch_t(const Shape &s, const AttnArgs &a, hipStream_t st) {
   const long items = (long)s.hq * s.nb;
   const int xcd = (s.hkv <= 8 && 8 % s.hkv == 0 && items % 8 == 0) ? 1 : 0;
-  hipLaunchKernelGGL((attn_mfma_kernel<DT, D, BLK>), dim3((unsigned)items), dim3(BLK * 2), 0, st,
-                     (const uint8_t *)a.q, (const uint8_t *)a.k, (const uint8_t *)a.v, a.kv_idx,
-                     a.kv_cnt, (uint16_t *)a.o, a.lse, a.q_scale, a.k_scale, a.v_scale, s.hq,
-                     s.hkv, s.seq, s.nb, a.sm_scale * kLog2e, xcd);
+  hipLaunchKernelGGL((attn_mfma_kernel<DT, D, BLK, false>), dim3((unsigned)items), dim3(BLK * 2),
+                     0, st, (const uint8_t *)a.q, (const uint8_t *)a.k, (const uint8_t *)a.v,
+                     a.kv_idx, a.kv_cnt, (uint16_t *)a.o, a.lse, a.q_scale, a.k_scale, a.v_scale,
+                     s.hq, s.hkv, s.seq, s.nb, a.sm_scale * kLog2e, xcd, VarlenDev{});
+  return hipGetLastError();
+}
+
+// Varlen: s.seq = tokens in the packed batch, s.nb = query blocks in it.
+template <int DT, int D, int BLK>
+static hipError_t launch_vl_t(const Shape &s, const AttnArgs &a, const VarlenArgs &v,
+                              hipStream_t st) {
+  const long items = (long)s.hq * s.nb;
+  const int xcd = (s.hkv <= 8 && 8 % s.hkv == 0 && items % 8 == 0) ? 1 : 0;
+  const VarlenDev vd{v.cu_seqlens, v.cu_blocks, v.page_table, v.block_order,
+                     v.nseq,       v.max_pages, v.idx_stride};
+  hipLaunchKernelGGL((attn_mfma_kernel<DT, D, BLK, true>), dim3((unsigned)items), dim3(BLK * 2),
+                     0, st, (const uint8_t *)a.q, (const uint8_t *)a.k, (const uint8_t *)a.v,
+                     a.kv_idx, a.kv_cnt, (uint16_t *)a.o, a.lse, a.q_scale, a.k_scale, a.v_scale,
+                     s.hq, s.hkv, s.seq, s.nb, a.sm_scale * kLog2e, xcd, vd);
   return hipGetLastError();
 }
 
@@ -541,12 +607,27 @@ static hipError_t launch_dt(const Shape &s, const AttnArgs &a, hipStream_t st) {
   return launch_t<DT, 128, 128>(s, a, st);
 }
 
+template <int DT>
+static hipError_t launch_vl_dt(const Shape &s, const AttnArgs &a, const VarlenArgs &v,
+                               hipStream_t st) {
+  if (s.d == 64 && s.block == 64) return launch_vl_t<DT, 64, 64>(s, a, v, st);
+  if (s.d == 64 && s.block == 128) return launch_vl_t<DT, 64, 128>(s, a, v, st);
+  if (s.d == 128 && s.block == 64) return launch_vl_t<DT, 128, 64>(s, a, v, st);
+  return launch_vl_t<DT, 128, 128>(s, a, v, st);
+}
+
 hipError_t launch_attn_bf16(const Shape &s, const AttnArgs &a, hipStream_t st) {
   return launch_dt<kBF16>(s, a, st);
 }
 
 hipError_t launch_attn_fp8(const Shape &s, const AttnArgs &a, hipStream_t st) {
   return launch_dt<kFP8>(s, a, st);
+}
+
+hipError_t launch_attn_varlen(const Shape &s, const AttnArgs &a, const VarlenArgs &v,
+                              hipStream_t st) {
+  if (s.dtype == kBF16) return launch_vl_dt<kBF16>(s, a, v, st);
+  return launch_vl_dt<kFP8>(s, a, v, st);
 }
 
 }  // namespace bsp

@@ -215,6 +215,42 @@ bsp_status bsp_calibrate_gamma(const bsp_desc *desc, const float *score, float t
   return BSP_OK;
 }
 
+bsp_status bsp_attn_fwd_varlen(const bsp_desc *desc, const bsp_varlen *vl, const void *q,
+                               const void *k_cache, const void *v_cache, const int32_t *kv_idx,
+                               const int32_t *kv_cnt, void *o, float *lse, void *stream) {
+  bsp_status st = check_desc(desc, true);
+  if (st != BSP_OK) return st;
+  if (!vl) return BSP_ERR_NULL_POINTER;
+  if (vl->nseq < 1 || vl->total_blocks < 0 || vl->max_pages < 1 || vl->idx_stride < 1)
+    return BSP_ERR_BAD_SHAPE;
+  if ((long)desc->hq * vl->total_blocks > 0x7fffffffL) return BSP_ERR_BAD_SHAPE;
+  if (desc->dtype == BSP_DTYPE_F32) return BSP_ERR_UNSUPPORTED;
+  if (desc->seq == 0 || vl->total_blocks == 0) return BSP_OK;
+  if (!vl->cu_seqlens || !vl->cu_blocks || !vl->page_table) return BSP_ERR_NULL_POINTER;
+  if (!q || !k_cache || !v_cache || !o) return BSP_ERR_NULL_POINTER;
+  if ((kv_idx == nullptr) != (kv_cnt == nullptr)) return BSP_ERR_NULL_POINTER;
+  const bool fp8 = desc->dtype == BSP_DTYPE_FP8_E4M3;
+  if (fp8 && (!desc->q_scale || !desc->k_scale || !desc->v_scale)) return BSP_ERR_BAD_DTYPE;
+  if (!fp8 && (desc->q_scale || desc->k_scale || desc->v_scale)) return BSP_ERR_BAD_DTYPE;
+  Shape s = shape_of(desc);
+  s.nb = vl->total_blocks;
+  bsp::AttnArgs a;
+  a.q = q;
+  a.k = k_cache;
+  a.v = v_cache;
+  a.kv_idx = kv_idx;
+  a.kv_cnt = kv_cnt;
+  a.q_scale = desc->q_scale;
+  a.k_scale = desc->k_scale;
+  a.v_scale = desc->v_scale;
+  a.o = o;
+  a.lse = lse;
+  a.sm_scale = scale_of(desc);
+  bsp::VarlenArgs v{vl->cu_seqlens, vl->cu_blocks, vl->page_table, vl->block_order,
+                    vl->nseq,       vl->max_pages, vl->idx_stride};
+  return hip_status(bsp::launch_attn_varlen(s, a, v, (hipStream_t)stream));
+}
+
 const char *bsp_status_string(int32_t status) {
   switch (status) {
     case BSP_OK: return "BSP_OK";

@@ -34,7 +34,14 @@ hipError_t launch_mask(const Shape &s, float gamma, int sink_blocks, int local_b
                        const float *score, const uint8_t *user_mask, uint8_t *mask,
                        int32_t *kv_idx, int32_t *kv_cnt, hipStream_t st,
                        const float *rescue = nullptr, float gamma_r = 0.f);
+struct VarlenArgs {
+  const int32_t *cu_seqlens, *cu_blocks, *page_table, *block_order;
+  int nseq, max_pages, idx_stride;
+};
+
 hipError_t launch_attn_f32(const Shape &s, const AttnArgs &a, hipStream_t st);
+hipError_t launch_attn_varlen(const Shape &s, const AttnArgs &a, const VarlenArgs &v,
+                              hipStream_t st);
 hipError_t launch_attn_bf16(const Shape &s, const AttnArgs &a, hipStream_t st);
 hipError_t launch_attn_fp8(const Shape &s, const AttnArgs &a, hipStream_t st);
 

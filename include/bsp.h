@@ -44,7 +44,7 @@
 extern "C" {
 #endif
 
-#define BSP_ABI_VERSION 4
+#define BSP_ABI_VERSION 5
 
 typedef enum bsp_status {
   BSP_OK = 0,
@@ -239,6 +239,49 @@ bsp_status bsp_attn_fwd(const bsp_desc *desc, const void *q, const void *k, cons
 bsp_status bsp_calibrate_gamma(const bsp_desc *desc, const float *score, float target, float tol,
                                uint8_t *mask, int32_t *kv_idx, int32_t *kv_cnt, int32_t *cnt_host,
                                float *gamma_out, float *density_out, void *stream);
+
+/*
+ * Packed variable-length batch over a paged K/V cache (FlashPrefill V2
+ * abstract on the thelatestinai page: paged KV cache and continuous batching
+ * for serving).  Sequence s owns tokens cu_seqlens[s] .. cu_seqlens[s+1] of
+ * q, o and lse ([heads][desc->seq][d], desc->seq = total tokens) and query
+ * blocks cu_blocks[s] .. cu_blocks[s+1] (ceil(len_s / block) of them).  Its
+ * key block J lives in cache page page_table[s][J]; the caches are laid out
+ * [pages][hkv][block][d] in the storage dtype (one page = one key block).
+ * The device arrays are the caller's contract (the host never reads them):
+ * cu_seqlens[0] = 0, nondecreasing, cu_seqlens[nseq] = desc->seq;
+ * cu_blocks[0] = 0, cu_blocks[nseq] = total_blocks; every page index valid.
+ */
+typedef struct {
+  const int32_t *cu_seqlens;  /* device [nseq + 1] */
+  const int32_t *cu_blocks;   /* device [nseq + 1] */
+  const int32_t *page_table;  /* device [nseq][max_pages] */
+  int32_t nseq;               /* >= 1 */
+  int32_t total_blocks;       /* query blocks in the batch, >= 0 */
+  int32_t max_pages;          /* row length of page_table, >= 1 */
+  int32_t idx_stride;         /* row stride of kv_idx, >= 1 (>= a sequence's block count) */
+  const int32_t *block_order; /* device [total_blocks], optional: a permutation of the batch's
+                                 query blocks in launch order (heaviest first balances the
+                                 tail); NULL = descending batch index */
+} bsp_varlen;
+
+/*
+ * bsp_attn_fwd_varlen - bsp_attn_fwd for a packed batch over a paged cache.
+ * Per sequence, exactly bsp_attn_fwd on its own tokens: query block I of
+ * sequence s and head h reads its kept key blocks (indices local to s, in
+ * [0, I]) from kv_idx[(h * total_blocks + cu_blocks[s] + I) * idx_stride ..]
+ * with count kv_cnt[h * total_blocks + cu_blocks[s] + I]; both NULL = dense
+ * causal.  A sequence's last page may be partly filled: rows past the
+ * sequence end are never read.
+ *
+ * q:        device [hq][desc->seq][d], storage dtype (bf16 or fp8)
+ * k_cache, v_cache: device [pages][hkv][block][d], storage dtype
+ * o, lse:   as for bsp_attn_fwd, over the packed tokens
+ * fp32 inputs return BSP_ERR_UNSUPPORTED.
+ */
+bsp_status bsp_attn_fwd_varlen(const bsp_desc *desc, const bsp_varlen *vl, const void *q,
+                               const void *k_cache, const void *v_cache, const int32_t *kv_idx,
+                               const int32_t *kv_cnt, void *o, float *lse, void *stream);
 
 /* Static description of a status code (host, never NULL). */
 const char *bsp_status_string(int32_t status);

@@ -27,9 +27,9 @@ def built():
 
 
 def test_header_declares_the_entry_points():
-    assert _declared() == ["bsp_abi_version", "bsp_attn_fwd", "bsp_calibrate_gamma", "bsp_mask",
-                           "bsp_mask_dual", "bsp_score", "bsp_score_arith", "bsp_score_rescue",
-                           "bsp_status_string"]
+    assert _declared() == ["bsp_abi_version", "bsp_attn_fwd", "bsp_attn_fwd_varlen",
+                           "bsp_calibrate_gamma", "bsp_mask", "bsp_mask_dual", "bsp_score",
+                           "bsp_score_arith", "bsp_score_rescue", "bsp_status_string"]
 
 
 def test_library_exports_every_declared_symbol():
@@ -156,3 +156,21 @@ def test_rescue_entry_points_host_checks():
     assert bsp.bsp_mask_dual(d, fake, None, 0.5, fake, fake, fake, None) == 1
     d0 = bsp.desc(4, 1, 0, 64, 64, bsp.DTYPE_BF16)
     assert bsp.bsp_score_rescue(d0, None, None, None, None, None, None) == 0
+
+
+def test_varlen_host_checks():
+    fake = 0x1000  # never dereferenced: every case fails before a launch
+    d = bsp.desc(4, 1, 1024, 64, 64, bsp.DTYPE_BF16)
+    ok = dict(cu_seqlens=fake, cu_blocks=fake, page_table=fake, nseq=2, total_blocks=16,
+              max_pages=16, idx_stride=16)
+    call = lambda dd, **kw: bsp.bsp_attn_fwd_varlen(dd, bsp.BspVarlen(**{**ok, **kw}), fake, fake,
+                                                    fake, None, None, fake, None, None)
+    assert call(d, nseq=0) == 2
+    assert call(d, total_blocks=-1) == 2
+    assert call(d, max_pages=0) == 2
+    assert call(d, page_table=None) == 1
+    assert call(bsp.desc(4, 1, 1024, 64, 64, bsp.DTYPE_F32)) == 5
+    assert call(d, total_blocks=0) == 0
+    assert bsp.lib().bsp_attn_fwd_varlen(ctypes.byref(d), None, fake, fake, fake, None, None,
+                                         fake, None, None) == 1
+    assert ctypes.sizeof(bsp.BspVarlen) == 3 * 8 + 4 * 4 + 8

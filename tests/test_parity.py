@@ -234,6 +234,76 @@ def test_long_rows_over_2048_blocks():
                 omd, ocntd)
 
 
+_NAN_BITS = {"bf16": 0x7FC0, "fp8": 0x7F}
+
+
+def _varlen_case(dtype, d, block, lens, seed, density):
+    """One generated batch split along tokens into sequences; K/V written into
+    a shuffled paged cache whose unused rows hold NaN bits; random masks."""
+    c = gen.make_case(4, 2, sum(lens), d, block, dtype, seed, rope=True, n_vert=4)
+    rng = np.random.default_rng(seed)
+    nbs = [-(-n // block) for n in lens]
+    tb = sum(nbs)
+    npages = tb + 7
+    perm = rng.permutation(npages).astype(np.int32)
+    kc = np.full((npages, c.hkv, block, d), _NAN_BITS[dtype], c.k.dtype)
+    vc = np.full_like(kc, _NAN_BITS[dtype])
+    ptab = np.zeros((len(lens), max(nbs) + 2), np.int32)
+    masks, t0, b0 = [], 0, 0
+    for s, (n, nb) in enumerate(zip(lens, nbs)):
+        for J in range(nb):
+            pg = perm[b0 + J]
+            ptab[s, J] = pg
+            r1 = min(block, n - J * block)
+            kc[pg, :, :r1] = c.k[:, t0 + J * block:t0 + J * block + r1]
+            vc[pg, :, :r1] = c.v[:, t0 + J * block:t0 + J * block + r1]
+        masks.append(gen.random_block_mask(c.hq, nb, density, seed + s))
+        t0 += n
+        b0 += nb
+    return c, kc, vc, ptab, masks, nbs
+
+
+@pytest.mark.parametrize("dtype,d,block,dense", [("bf16", 128, 128, False), ("bf16", 128, 128, True),
+                                                  ("bf16", 64, 64, False), ("fp8", 128, 128, False),
+                                                  ("fp8", 64, 64, True)])
+def test_varlen_paged_matches_oracle_per_sequence(dtype, d, block, dense):
+    lens = [1000, 130, 512, 64, 777, 1]
+    announce(f"varlen paged {dtype} d={d} B={block} dense={dense} lens={lens}")
+    c, kc, vc, ptab, masks, nbs = _varlen_case(dtype, d, block, lens, 31 + d + block, 0.5)
+    dv = H.dev(c)
+    t = lambda x: (torch.from_numpy(x.view(np.int16)).cuda().view(torch.bfloat16) if dtype == "bf16"
+                   else torch.from_numpy(x).cuda())
+    kv_idx = kv_cnt = None
+    if not dense:
+        stride = max(nbs) + 3
+        tb = sum(nbs)
+        idx = np.full((c.hq, tb, stride), -7, np.int32)
+        cnt = np.zeros((c.hq, tb), np.int32)
+        b0 = 0
+        for m, nb in zip(masks, nbs):
+            i_s, c_s = H.idx_from_mask(m)
+            idx[:, b0:b0 + nb, :nb] = np.where(i_s >= 0, i_s, -7)
+            cnt[:, b0:b0 + nb] = c_s
+            b0 += nb
+        kv_idx, kv_cnt = torch.from_numpy(idx).cuda(), torch.from_numpy(cnt).cuda()
+    o, lse = bsp.attn_fwd_varlen(dv["q"], t(kc), t(vc), torch.from_numpy(ptab).cuda(), lens, block,
+                                 kv_idx, kv_cnt, q_scale=dv["q_scale"], k_scale=dv["k_scale"],
+                                 v_scale=dv["v_scale"])
+    torch.cuda.synchronize()
+    go, gl = o.float().cpu().numpy(), lse.cpu().numpy()
+    assert np.all(np.isfinite(go))
+    t0, err = 0, 0.0
+    for n, nb, m in zip(lens, nbs, masks):
+        sl = slice(t0, t0 + n)
+        mm = np.tril(np.ones((c.hq, nb, nb), np.uint8)) if dense else m
+        oo, ol = oracle.attn(c.q[:, sl], c.k[:, sl], c.v[:, sl], dtype, block, mm,
+                             q_scale=c.q_scale, k_scale=c.k_scale, v_scale=c.v_scale)
+        err = max(err, H.check_attn(go[:, sl].reshape(-1, d), gl[:, sl].reshape(-1),
+                                    oo.reshape(-1, d), ol.reshape(-1), dtype))
+        t0 += n
+    print(f"  max-abs O err {err:.2e}", flush=True)
+
+
 @pytest.mark.parametrize("which,target", [("s1_0", 0.3), ("s1_1", 0.7), ("llama_4k", 0.7)])
 def test_calibrate_gamma_matches_oracle(which, target):
     """Bisection on the GPU masks lands on the oracle's gamma; the buffers
