@@ -13,7 +13,9 @@
 //   * Workgroups are numbered heaviest row first and, when the kv heads divide
 //     the 8 XCDs evenly, every XCD serves whole GQA groups: the 64 workgroups
 //     resident on an XCD walk the same K/V blocks in the same order, so K/V
-//     come from that XCD's L2.
+//     come from that XCD's L2.  When the K/V of all groups would overflow
+//     the memory-side cache, the groups go in phases of fewer at a time, so
+//     blocks that miss L2 (scattered kept blocks) are served from it.
 //   * Scores are computed transposed in 16x16 tiles, S^T = K Q^T
 //     (v_mfma_f32_16x16x32_bf16, or one v_mfma_scale_f32_16x16x128_f8f6f4
 //     with unit scales per tile for e4m3).  Lane 16g + r owns query r of each
@@ -387,7 +389,7 @@ struct VarlenDev {
 };
 
 template <int DT, int D, int BLK, bool VL>
-__global__ __launch_bounds__(BLK * 2, 256 / BLK) void attn_mfma_kernel(
+__global__ __launch_bounds__(BLK * 2, (BLK == 64 && D == 128) ? 1 : 2) void attn_mfma_kernel(
     const uint8_t *__restrict__ q, const uint8_t *__restrict__ k, const uint8_t *__restrict__ v,
     const int32_t *__restrict__ kv_idx, const int32_t *__restrict__ kv_cnt,
     uint16_t *__restrict__ o, float *__restrict__ lse, const float *__restrict__ q_scale,
@@ -411,7 +413,19 @@ __global__ __launch_bounds__(BLK * 2, 256 / BLK) void attn_mfma_kernel(
   int I, h;
   {
     const int bid = blockIdx.x;
-    if (xcd_map) {
+    if (xcd_map > 0 && xcd_map < hkv) {
+      // Phases of P = xcd_map kv groups, so that the K/V of the groups in
+      // flight stay within the memory-side cache: in phase p, XCD x serves
+      // group p * P + x / S (S = 8 / P XCDs per group) and, of that group,
+      // the rows I with (nb - 1 - I) % S == x % S, all q heads of the group,
+      // heaviest row first.
+      const int P = xcd_map, S = 8 / P;
+      const int x = bid & 7, j = bid >> 3;
+      const int len = grp * nb / S;
+      const int p = j / len, jj = j - p * len;
+      I = nb - 1 - (x % S + S * (jj / grp));
+      h = (p * P + x / S) * grp + jj % grp;
+    } else if (xcd_map) {
       // XCD x = bid % 8 serves kv group x % hkv; its workgroups walk the
       // group's (row, head) items heaviest row first.
       const int x = bid & 7, j = bid >> 3, X = 8 / hkv;
@@ -573,10 +587,25 @@ __global__ __launch_bounds__(BLK * 2, 256 / BLK) void attn_mfma_kernel(
   }
 }
 
+// Workgroup order (see the kernel): 0 = plain heaviest-first; hkv or more =
+// every XCD serves whole kv groups, all groups at once; 1 .. hkv-1 = that many
+// groups in flight at a time.  Groups go in phases when the K/V of all of
+// them exceed half of the 256 MiB memory-side cache, which then keeps the
+// K/V of the groups in flight for the blocks that miss the XCD's L2 (many
+// when kept blocks are scattered); the dense order is unaffected by it.
+static int xcd_mode(const Shape &s, long kv_bytes_per_group) {
+  const long items = (long)s.hq * s.nb;
+  if (!(s.hkv <= 8 && 8 % s.hkv == 0 && items % 8 == 0)) return 0;
+  int P = s.hkv;
+  while (P > 1 && (long)P * kv_bytes_per_group > (128l << 20)) P >>= 1;
+  if (P < s.hkv && s.nb % (8 / P) != 0) P = s.hkv;
+  return P;
+}
+
 template <int DT, int D, int BLK>
 static hipError_t launch_t(const Shape &s, const AttnArgs &a, hipStream_t st) {
   const long items = (long)s.hq * s.nb;
-  const int xcd = (s.hkv <= 8 && 8 % s.hkv == 0 && items % 8 == 0) ? 1 : 0;
+  const int xcd = xcd_mode(s, 2l * s.seq * D * (DT == kFP8 ? 1 : 2));
   hipLaunchKernelGGL((attn_mfma_kernel<DT, D, BLK, false>), dim3((unsigned)items), dim3(BLK * 2),
                      0, st, (const uint8_t *)a.q, (const uint8_t *)a.k, (const uint8_t *)a.v,
                      a.kv_idx, a.kv_cnt, (uint16_t *)a.o, a.lse, a.q_scale, a.k_scale, a.v_scale,
@@ -589,7 +618,8 @@ template <int DT, int D, int BLK>
 static hipError_t launch_vl_t(const Shape &s, const AttnArgs &a, const VarlenArgs &v,
                               hipStream_t st) {
   const long items = (long)s.hq * s.nb;
-  const int xcd = (s.hkv <= 8 && 8 % s.hkv == 0 && items % 8 == 0) ? 1 : 0;
+  // a row reads only its own sequence's pages: all groups at once
+  const int xcd = xcd_mode(s, 0);
   const VarlenDev vd{v.cu_seqlens, v.cu_blocks, v.page_table, v.block_order,
                      v.nseq,       v.max_pages, v.idx_stride};
   hipLaunchKernelGGL((attn_mfma_kernel<DT, D, BLK, true>), dim3((unsigned)items), dim3(BLK * 2),
