@@ -42,8 +42,7 @@
 
 #include <type_traits>
 
-#include "device.h"
-#include "internal.h"
+#include "attn_common.h"
 
 namespace bsp {
 
@@ -98,21 +97,6 @@ __device__ __forceinline__ int v_chunk(int r, int c) {
 }
 
 
-
-// Buffer descriptor over [base, base + bytes): raw (stride 0), untyped
-// 32-bit data format as gfx9-family untyped buffer loads expect.
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, uint32_t bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes,
-                                           0x00020000);
-}
-
-// 16 bytes per lane from rsrc + soff + voff straight into LDS at ldst + 16 * lane
-// (buffer_load_dwordx4 ... lds): no VGPR staging and no 64-bit address math.
-__device__ __forceinline__ void lds_dma16(__amdgpu_buffer_rsrc_t rs, uint32_t voff, uint32_t soff,
-                                          void *ldst) {
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (__attribute__((address_space(3))) void *)ldst, 16,
-                                           voff, soff, 0, 0);
-}
 
 template <int DT, int D, int BLK>
 struct Attn {
@@ -379,15 +363,6 @@ struct Attn {
   }
 };
 
-// Packed variable-length batch over a paged K/V cache (VL): sequence s owns
-// tokens cu_seqlens[s] .. cu_seqlens[s+1] of q / o / lse and query blocks
-// cu_blocks[s] .. cu_blocks[s+1] of the grid; key block J of sequence s is
-// cache page page_table[s * max_pages + J], laid out [page][hkv][BLK][d].
-struct VarlenDev {
-  const int32_t *cu_seqlens, *cu_blocks, *page_table, *block_order;
-  int nseq, max_pages, idx_stride;
-};
-
 template <int DT, int D, int BLK, bool VL>
 __global__ __launch_bounds__(BLK * 2, (BLK == 64 && D == 128) ? 1 : 2) void attn_mfma_kernel(
     const uint8_t *__restrict__ q, const uint8_t *__restrict__ k, const uint8_t *__restrict__ v,
@@ -411,52 +386,15 @@ __global__ __launch_bounds__(BLK * 2, (BLK == 64 && D == 128) ? 1 : 2) void attn
   T.r16 = T.lane & 15;
   const int grp = hq / hkv;
   int I, h;
-  {
-    const int bid = blockIdx.x;
-    if (xcd_map > 0 && xcd_map < hkv) {
-      // Phases of P = xcd_map kv groups, so that the K/V of the groups in
-      // flight stay within the memory-side cache: in phase p, XCD x serves
-      // group p * P + x / S (S = 8 / P XCDs per group) and, of that group,
-      // the rows I with (nb - 1 - I) % S == x % S, all q heads of the group,
-      // heaviest row first.
-      const int P = xcd_map, S = 8 / P;
-      const int x = bid & 7, j = bid >> 3;
-      const int len = grp * nb / S;
-      const int p = j / len, jj = j - p * len;
-      I = nb - 1 - (x % S + S * (jj / grp));
-      h = (p * P + x / S) * grp + jj % grp;
-    } else if (xcd_map) {
-      // XCD x = bid % 8 serves kv group x % hkv; its workgroups walk the
-      // group's (row, head) items heaviest row first.
-      const int x = bid & 7, j = bid >> 3, X = 8 / hkv;
-      const int n = x / hkv + X * j;
-      I = nb - 1 - n / grp;
-      h = (x % hkv) * grp + n % grp;
-    } else {
-      I = nb - 1 - bid / hq;
-      h = bid % hq;
-    }
-  }
+  attn_row_of(blockIdx.x, xcd_map, hq, hkv, nb, I, h);
   const int g = h / grp;
   // token rows of q / o / lse: ntok per head, this sequence from tok0; len
-  // tokens in this sequence; the kv list row and its stride
+  // tokens in this sequence; the kv list row gb and its stride
   const int ntok = seq;
-  int len = seq, tok0 = 0, gb = I, stride = nb;
-  const int32_t *ptab = nullptr;
-  if constexpr (VL) {
-    // launch order: the caller's permutation (heaviest first), if given
-    if (vl.block_order) gb = vl.block_order[nb - 1 - I];
-    int lo = 0, hi = vl.nseq;  // the sequence whose blocks contain gb
-    while (hi - lo > 1) {
-      const int mid = (lo + hi) >> 1;
-      if (vl.cu_blocks[mid] <= gb) lo = mid; else hi = mid;
-    }
-    I = gb - vl.cu_blocks[lo];
-    tok0 = vl.cu_seqlens[lo];
-    len = vl.cu_seqlens[lo + 1] - tok0;
-    ptab = vl.page_table + (size_t)lo * vl.max_pages;
-    stride = vl.idx_stride;
-  }
+  const AttnRow R = attn_locate<VL>(I, seq, nb, vl);
+  I = R.I;
+  const int len = R.len, tok0 = R.tok0, gb = R.gb, stride = R.stride;
+  const int32_t *ptab = R.ptab;
   T.I = I;
   T.seq = len;
   T.k = k;
@@ -511,29 +449,10 @@ __global__ __launch_bounds__(BLK * 2, (BLK == 64 && D == 128) ? 1 : 2) void attn
   T.l[0] = T.l[1] = 0.f;
 
   const int nblk = kv_idx ? max(0, min(kv_cnt[row], stride)) : I + 1;
-  const int32_t *ilist = kv_idx ? kv_idx + row * stride : nullptr;
   const int ns = nblk * NSUB;
-  // The kv list streams through registers 64 entries at a time: lane l holds
-  // entry 64c + l of chunk c, and chunk c + 1 is loaded on entering chunk c.
-  // An entry is picked with readlane, so no step waits on a global load of
-  // its block index (such waits desynchronise the workgroups that otherwise
-  // walk the same K/V blocks together out of L2).  Invalid entries are skipped.
-  int lcur = 0, lnxt = 0, chunk = 0;
-  if (ilist) {
-    lcur = T.lane < nblk ? ilist[T.lane] : 0;
-    lnxt = 64 + T.lane < nblk ? ilist[64 + T.lane] : 0;
-  }
-  auto block_of = [&](int t) -> int {
-    if (!ilist) return t;
-    if ((t >> 6) != chunk) {  // t grows by at most one per call
-      chunk = t >> 6;
-      lcur = lnxt;
-      const int e = (chunk + 1) * 64 + T.lane;
-      lnxt = e < nblk ? ilist[e] : 0;
-    }
-    const int J = __builtin_amdgcn_readlane(lcur, t & 63);
-    return (J < 0 || J > I) ? -1 : J;
-  };
+  KvStream kv;
+  kv.init(kv_idx ? kv_idx + row * stride : nullptr, nblk, I, T.lane);
+  auto block_of = [&](int t) { return kv.block_of(t); };
 
   // Pipeline: step i waits for sub-tile i (issued one step earlier), passes a
   // barrier, issues sub-tile i+1 into the other buffer and computes i.
@@ -587,25 +506,10 @@ __global__ __launch_bounds__(BLK * 2, (BLK == 64 && D == 128) ? 1 : 2) void attn
   }
 }
 
-// Workgroup order (see the kernel): 0 = plain heaviest-first; hkv or more =
-// every XCD serves whole kv groups, all groups at once; 1 .. hkv-1 = that many
-// groups in flight at a time.  Groups go in phases when the K/V of all of
-// them exceed half of the 256 MiB memory-side cache, which then keeps the
-// K/V of the groups in flight for the blocks that miss the XCD's L2 (many
-// when kept blocks are scattered); the dense order is unaffected by it.
-static int xcd_mode(const Shape &s, long kv_bytes_per_group) {
-  const long items = (long)s.hq * s.nb;
-  if (!(s.hkv <= 8 && 8 % s.hkv == 0 && items % 8 == 0)) return 0;
-  int P = s.hkv;
-  while (P > 1 && (long)P * kv_bytes_per_group > (128l << 20)) P >>= 1;
-  if (P < s.hkv && s.nb % (8 / P) != 0) P = s.hkv;
-  return P;
-}
-
 template <int DT, int D, int BLK>
 static hipError_t launch_t(const Shape &s, const AttnArgs &a, hipStream_t st) {
   const long items = (long)s.hq * s.nb;
-  const int xcd = xcd_mode(s, 2l * s.seq * D * (DT == kFP8 ? 1 : 2));
+  const int xcd = attn_xcd_mode(s, 2l * s.seq * D * (DT == kFP8 ? 1 : 2));
   hipLaunchKernelGGL((attn_mfma_kernel<DT, D, BLK, false>), dim3((unsigned)items), dim3(BLK * 2),
                      0, st, (const uint8_t *)a.q, (const uint8_t *)a.k, (const uint8_t *)a.v,
                      a.kv_idx, a.kv_cnt, (uint16_t *)a.o, a.lse, a.q_scale, a.k_scale, a.v_scale,
@@ -619,7 +523,7 @@ static hipError_t launch_vl_t(const Shape &s, const AttnArgs &a, const VarlenArg
                               hipStream_t st) {
   const long items = (long)s.hq * s.nb;
   // a row reads only its own sequence's pages: all groups at once
-  const int xcd = xcd_mode(s, 0);
+  const int xcd = attn_xcd_mode(s, 0);
   const VarlenDev vd{v.cu_seqlens, v.cu_blocks, v.page_table, v.block_order,
                      v.nseq,       v.max_pages, v.idx_stride};
   hipLaunchKernelGGL((attn_mfma_kernel<DT, D, BLK, true>), dim3((unsigned)items), dim3(BLK * 2),
