@@ -46,9 +46,9 @@ __global__ __launch_bounds__(BLK * 2) void score_arith_kernel(
     const float *__restrict__ q_scale, int hq, int hkv, int seq, int nb, float c2) {
   using C = ArithCfg<DT, D, BLK>;
   constexpr int NW = C::NW, NT = C::NT, KS = C::KS, RSB = C::RSB, RSF = C::RSF;
-  __shared__ __attribute__((aligned(16))) uint8_t kt[C::LDSB];
-  __shared__ float qoff[BLK];       // per query: max + log2(sum) of pass 1
-  __shared__ float part[NW][32];    // per wavefront: sum of p over its queries
+  __shared__ __attribute__((aligned(16))) uint8_t ktb[2][C::LDSB];  // double-buffered tile
+  __shared__ float qoff[BLK];         // per query: max + log2(sum) of pass 1
+  __shared__ float part[2][NW][32];   // per wavefront: sum of p over its queries
 
   const int bid = blockIdx.x;
   const int I = nb - 1 - bid / hq, h = bid % hq;
@@ -96,45 +96,52 @@ __global__ __launch_bounds__(BLK * 2) void score_arith_kernel(
     }
   }
 
-  // ---- Kbar tile jt -> LDS (fp32, or three bf16 planes), whole workgroup
-  auto stage = [&](int jt) {
+  // ---- Kbar tile jt -> LDS (fp32, or three bf16 planes), whole workgroup:
+  //      the global loads of tile jt + 1 are issued before the MFMAs of tile
+  //      jt, the split and the LDS stores follow them
+  constexpr int FPT = 32 * D / 4 / NT;  // float4 per thread per tile
+  static_assert(FPT * NT * 4 == 32 * D, "tile staging");
+  float4 xr[FPT];
+  auto stage_load = [&](int jt) {
     const float *src = k_pool + ((size_t)g * nb + jt * 32) * D;
     const int n = min(32, nb - jt * 32);
-    for (int f = threadIdx.x; f < 32 * D / 4; f += NT) {
+#pragma unroll
+    for (int u = 0; u < FPT; ++u) {
+      const int f = threadIdx.x + u * NT;
+      xr[u] = f / (D / 4) < n ? *(const float4 *)(src + 4 * f) : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+  };
+  auto stage_store = [&](uint8_t *kt) {
+#pragma unroll
+    for (int u = 0; u < FPT; ++u) {
+      const int f = threadIdx.x + u * NT;
       const int r = f / (D / 4), c4 = (f % (D / 4)) * 4;
-      const float4 x = r < n ? *(const float4 *)(src + 4 * f) : make_float4(0.f, 0.f, 0.f, 0.f);
+      const float4 x = xr[u];
       if constexpr (C::F32) {
         *(float4 *)((float *)kt + r * RSF + c4) = x;
       } else {
+        // hi + mid + lo, each the bf16 rounding (to nearest even) of what the
+        // planes before it leave; every difference is exact in fp32
         const float xs[4] = {x.x, x.y, x.z, x.w};
-        uint32_t hp[2], mp[2], lp[2];
+        bf16x4 hv, mv, lv;
 #pragma unroll
-        for (int e = 0; e < 4; e += 2) {
-          uint32_t hb[2], mb[2], lb[2];
-#pragma unroll
-          for (int u = 0; u < 2; ++u) {
-            const float v = xs[e + u];
-            hb[u] = f32_to_bf16_bits(v);
-            const float r1 = v - bf16_bits_to_f32(hb[u]);
-            mb[u] = f32_to_bf16_bits(r1);
-            const float r2 = r1 - bf16_bits_to_f32(mb[u]);
-            lb[u] = f32_to_bf16_bits(r2);
-          }
-          hp[e / 2] = hb[0] | (hb[1] << 16);
-          mp[e / 2] = mb[0] | (mb[1] << 16);
-          lp[e / 2] = lb[0] | (lb[1] << 16);
+        for (int e = 0; e < 4; ++e) {
+          hv[e] = (__bf16)xs[e];
+          const float r1 = xs[e] - (float)hv[e];
+          mv[e] = (__bf16)r1;
+          lv[e] = (__bf16)(r1 - (float)mv[e]);
         }
         uint8_t *base = kt + r * RSB + c4 * 2;
-        *(uint2 *)(base) = make_uint2(hp[0], hp[1]);
-        *(uint2 *)(base + C::PLANE) = make_uint2(mp[0], mp[1]);
-        *(uint2 *)(base + 2 * C::PLANE) = make_uint2(lp[0], lp[1]);
+        __builtin_memcpy(base, &hv, 8);
+        __builtin_memcpy(base + C::PLANE, &mv, 8);
+        __builtin_memcpy(base + 2 * C::PLANE, &lv, 8);
       }
     }
   };
 
   // One 32 x 32 tile: kfirst ? S^T = Kbar Q^T : S = Q Kbar^T.  The Kbar
   // fragment of lane l is row l % 32 of the tile, the same for both orders.
-  auto tile = [&](bool kfirst) -> f32x16 {
+  auto tile = [&](const uint8_t *kt, bool kfirst) -> f32x16 {
     f32x16 acc = f32x16{};
     if constexpr (C::F32) {
       const float *arow = (const float *)kt + l32 * RSF + (D / 2) * half;
@@ -165,11 +172,12 @@ __global__ __launch_bounds__(BLK * 2) void score_arith_kernel(
 
   // ---- pass 1: per query, max and sum of exp2 over the causal key blocks
   float m = -INFINITY, l = 0.f;
+  stage_load(0);
+  stage_store(ktb[0]);
+  __syncthreads();
   for (int jt = 0; jt < ntile; ++jt) {
-    __syncthreads();
-    stage(jt);
-    __syncthreads();
-    const f32x16 acc = tile(true);
+    if (jt + 1 < ntile) stage_load(jt + 1);
+    const f32x16 acc = tile(ktb[jt & 1], true);
     float s[16], tmax = -INFINITY;
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
@@ -181,48 +189,59 @@ __global__ __launch_bounds__(BLK * 2) void score_arith_kernel(
     if (mn != -INFINITY) {
       float a = 0.f;
 #pragma unroll
-      for (int r = 0; r < 16; ++r) a += exp2f(s[r] - mn);
-      l = l * exp2f(m - mn) + a;
+      for (int r = 0; r < 16; ++r) a += __builtin_amdgcn_exp2f(s[r] - mn);
+      l = l * __builtin_amdgcn_exp2f(m - mn) + a;
       m = mn;
     }
+    if (jt + 1 < ntile) stage_store(ktb[(jt + 1) & 1]);
+    __syncthreads();
   }
   {
     const float mo = __shfl_xor(m, 32, 64), lo = __shfl_xor(l, 32, 64);
     const float mn = fmaxf(m, mo);
-    l = (m == -INFINITY ? 0.f : l * exp2f(m - mn)) + (mo == -INFINITY ? 0.f : lo * exp2f(mo - mn));
+    l = (m == -INFINITY ? 0.f : l * __builtin_amdgcn_exp2f(m - mn)) +
+        (mo == -INFINITY ? 0.f : lo * __builtin_amdgcn_exp2f(mo - mn));
     m = mn;
   }
   // a query past the end of the sequence gets +inf: its p is 0 in pass 2
   if (half == 0) qoff[w * 32 + l32] = qi < seq ? m + log2f(l) : INFINITY;
+  stage_load(0);
+  stage_store(ktb[0]);
   __syncthreads();
   // pass-2 rows of this lane: queries w*32 + (r/4)*8 + half*4 + r%4
   float off[16];
 #pragma unroll
   for (int r = 0; r < 16; ++r) off[r] = qoff[w * 32 + (r / 4) * 8 + half * 4 + (r % 4)];
 
-  // ---- pass 2: p = exp2(s - off) summed over the block's queries
+  // ---- pass 2: p = exp2(s - off) summed over the block's queries; wave 0
+  //      adds the wavefronts' sums of tile jt and writes them while tile
+  //      jt + 1 is computed
   const float invn = 1.f / (float)nvalid;
+  auto emit = [&](int jt) {
+    const int J = jt * 32 + l32;
+    if (w == 0 && half == 0 && J < nb) {
+      float t = 0.f;
+#pragma unroll
+      for (int i = 0; i < NW; ++i) t += part[jt & 1][i][l32];
+      prow[J] = J <= I ? t * invn : 0.f;
+    }
+  };
   for (int jt = 0; jt < ntile; ++jt) {
-    __syncthreads();
-    stage(jt);
-    __syncthreads();
-    const f32x16 acc = tile(false);
+    if (jt + 1 < ntile) stage_load(jt + 1);
+    const f32x16 acc = tile(ktb[jt & 1], false);
     const int J = jt * 32 + l32;
     float a = 0.f;
     if (J <= I) {
 #pragma unroll
-      for (int r = 0; r < 16; ++r) a += exp2f(acc[r] * scl - off[r]);
+      for (int r = 0; r < 16; ++r) a += __builtin_amdgcn_exp2f(acc[r] * scl - off[r]);
     }
     a += __shfl_xor(a, 32, 64);
-    if (half == 0) part[w][l32] = a;
+    if (half == 0) part[jt & 1][w][l32] = a;
+    if (jt > 0) emit(jt - 1);
+    if (jt + 1 < ntile) stage_store(ktb[(jt + 1) & 1]);
     __syncthreads();
-    if (w == 0 && half == 0 && J < nb) {
-      float t = 0.f;
-#pragma unroll
-      for (int i = 0; i < NW; ++i) t += part[i][l32];
-      prow[J] = J <= I ? t * invn : 0.f;
-    }
   }
+  emit(ntile - 1);
   // zeros past the causal tiles
   for (int J = ntile * 32 + threadIdx.x; J < nb; J += NT) prow[J] = 0.f;
 }
