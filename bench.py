@@ -37,7 +37,10 @@ sys.path.insert(0, ROOT)
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
 PEAK_FP8_TFLOPS = 5000.0    # MI355X dense fp8 MFMA
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
-ATTN_SRC = os.path.join(ROOT, "block_sparse_attention_bsp_amd", "csrc", "attn_mfma.hip")
+# the sources the attention kernel is compiled from, in the order they are
+# hashed for the counter note's source fingerprint
+ATTN_SRCS = [os.path.join(ROOT, "block_sparse_attention_bsp_amd", "csrc", f)
+             for f in ("attn_mfma.hip", "attn_common.h", "device.h", "internal.h")]
 PMC_NOTE = os.path.join(ROOT, "profiles", "attn_mfma_bf16_llama128k_pmc.md")
 
 
@@ -61,9 +64,9 @@ def parse():
                    help="add the radius-based rescue branch (bsp_score_rescue + bsp_mask_dual) "
                         "with this threshold factor")
     p.add_argument("--varlen", action="store_true",
-                   help="time bsp_attn_fwd_varlen instead: a packed batch of the config's heads "
-                        "with seeded lengths (log-uniform 1K-32K tokens, 128K in all) over a "
-                        "shuffled paged cache, dense causal per sequence")
+                   help="time the packed-batch path instead (bsp_score_varlen, bsp_mask_varlen, "
+                        "bsp_attn_fwd_varlen): the config's heads, seeded lengths (log-uniform "
+                        "1K-32K tokens, 128K in all) over a shuffled paged cache")
     p.add_argument("--calibrate", type=float, default=None, metavar="TARGET",
                    help="also time bsp_calibrate_gamma for this target density")
     p.add_argument("--copy-calibration", action="store_true",
@@ -109,7 +112,10 @@ def traffic_from_note():
     m_b = re.search(r"traffic_bytes_per_launch:\s*([0-9.eE+]+)", txt)
     if not m_sha or not m_b:
         return None
-    cur = hashlib.sha256(open(ATTN_SRC, "rb").read()).hexdigest()
+    h = hashlib.sha256()
+    for f in ATTN_SRCS:
+        h.update(open(f, "rb").read())
+    cur = h.hexdigest()
     return float(m_b.group(1)) if cur == m_sha.group(1) else None
 
 
@@ -141,14 +147,15 @@ def cpu_baseline(case, gpu_mask, nrows):
 
 
 def varlen_main(a):
-    """Paged variable-length attention on one packed batch (attention stage
-    only; each sequence dense causal)."""
+    """The whole path on one packed batch over a paged K/V cache:
+    bsp_score_varlen + bsp_mask_varlen + bsp_attn_fwd_varlen."""
     import torch
     import block_sparse_attention_bsp_amd as bsp
     import gen
     torch.cuda.set_device(0)
     cfg = gen.CONFIGS[a.config]
     hq, hkv, d, B = cfg["hq"], cfg["hkv"], cfg["d"], cfg["block"]
+    gamma = cfg["gamma"]
     rng = np.random.default_rng(2024)
     lens, total = [], 131072
     while sum(lens) < total:
@@ -172,34 +179,63 @@ def varlen_main(a):
     if cfg["dtype"] == "fp8":
         sc = {k: torch.ones(n, device="cuda") for k, n in
               (("q_scale", hq), ("k_scale", hkv), ("v_scale", hkv))}
-    run = lambda: bsp.attn_fwd_varlen(q, kc, vc, ptab, lens, B, **sc)
+    scs = {k: v for k, v in sc.items() if k != "v_scale"}
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+    st = {"score": 0.0, "mask": 0.0, "attn": 0.0}
+
+    def step(timed):
+        ev[0].record()
+        _, _, S = bsp.score_varlen(q, kc, ptab, lens, B, **scs)
+        ev[1].record()
+        _, idx, cnt = bsp.mask_varlen(S, gamma, lens, B, want_mask=False)
+        ev[2].record()
+        bsp.attn_fwd_varlen(q, kc, vc, ptab, lens, B, idx, cnt, **sc)
+        ev[3].record()
+        if timed:
+            torch.cuda.synchronize()
+            for k_, i in (("score", 0), ("mask", 1), ("attn", 2)):
+                st[k_] += ev[i].elapsed_time(ev[i + 1])
+        return cnt
+
     for _ in range(a.warmup):
-        run()
+        step(False)
     torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     t0 = time.perf_counter()
-    e0.record()
     for _ in range(a.steps):
-        run()
-    e1.record()
+        cnt = step(True)
     torch.cuda.synchronize()
-    ms = e0.elapsed_time(e1) / a.steps
     wall = (time.perf_counter() - t0) * 1e3 / a.steps
+    st = {k_: v / a.steps for k_, v in st.items()}
+    ms = sum(st.values())
+    # kept work: causal token pairs of every kept (row, key block) pair, the
+    # ragged last block of each sequence counted with its valid tokens
+    mk, _, _ = bsp.mask_varlen(bsp.score_varlen(q, kc, ptab, lens, B, **scs)[2], gamma, lens, B)
+    m = mk.cpu().numpy().astype(bool)
+    pairs, cb = 0.0, 0
+    for n, nb in zip(lens, nbs):
+        tok = np.minimum(B, n - B * np.arange(nb)).astype(np.float64)
+        w = np.outer(tok, tok)
+        w[np.diag_indices(nb)] = tok * (tok + 1) / 2
+        pairs += (m[:, cb:cb + nb, :nb] * w[None]).sum()
+        cb += nb
+    F_kept = 4.0 * d * pairs
     F = sum(dense_flops(hq, n, d) for n in lens)
+    dens = float(m.sum()) / sum(hq * nb * (nb + 1) / 2 for nb in nbs)
     peak = PEAK_FP8_TFLOPS if cfg["dtype"] == "fp8" else PEAK_BF16_TFLOPS
-    tf = F / (ms * 1e-3) / 1e12
+    ach = F_kept / (st["attn"] * 1e-3) / 1e12
     print(json.dumps({
-        "metric": "paged varlen prefill-attn TFLOP/s (dense causal per sequence)",
-        "value": round(tf, 3), "unit": "TFLOP/s", "n_gpus": 1, "steps": a.steps,
-        "warmup": a.warmup, "ms_per_step": round(wall, 4), "higher_is_better": True,
-        "scaling": "weak", "vs_baseline": None, "dtype": cfg["dtype"],
+        "metric": "paged varlen prefill ms per batch + effective TFLOP/s (dense causal per sequence)",
+        "value": round(F / (ms * 1e-3) / 1e12, 3), "unit": "TFLOP/s", "n_gpus": 1,
+        "steps": a.steps, "warmup": a.warmup, "ms_per_step": round(wall, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": cfg["dtype"],
         "data": "synthetic (random N(0,1) q and paged K/V, seeded length mix)",
         "config": {"workload": f"{len(lens)} sequences, {ntok} tokens, {hq} q / {hkv} kv heads, "
-                               f"d {d}, block {B}, pages shuffled", "lengths": lens},
-        "attn_ms": round(ms, 4),
-        "roofline": {"bound": "mfma", "achieved": round(tf, 3), "peak": peak,
-                     "unit": "TFLOP/s", "frac": round(tf / peak, 4), "traffic": None,
-                     "kernel": "attn_mfma_kernel (varlen)", "flops_per_launch": F},
+                               f"d {d}, block {B}, gamma {gamma}, pages shuffled",
+                   "lengths": lens},
+        "stage_ms": {k_: round(v, 4) for k_, v in st.items()}, "density": round(dens, 6),
+        "roofline": {"bound": "mfma", "achieved": round(ach, 3), "peak": peak,
+                     "unit": "TFLOP/s", "frac": round(ach / peak, 4), "traffic": None,
+                     "kernel": "attn_mfma_kernel (varlen)", "flops_per_launch": F_kept},
     }), flush=True)
 
 

@@ -23,7 +23,8 @@ __all__ = [
     "BspError", "BspDesc", "lib", "library_path", "desc", "score", "mask", "attn_fwd", "prefill",
     "calibrate_gamma", "score_arith", "score_rescue", "mask_dual", "bsp_score", "bsp_score_arith",
     "bsp_score_rescue", "bsp_mask", "bsp_mask_dual", "bsp_attn_fwd", "bsp_calibrate_gamma",
-    "BspVarlen", "bsp_attn_fwd_varlen", "attn_fwd_varlen",
+    "BspVarlen", "bsp_attn_fwd_varlen", "attn_fwd_varlen", "bsp_score_varlen", "bsp_mask_varlen",
+    "score_varlen", "mask_varlen", "prefill_varlen",
     "bsp_status_string", "bsp_abi_version",
     "DTYPE_F32", "DTYPE_BF16", "DTYPE_FP8_E4M3",
 ]
@@ -84,12 +85,14 @@ def lib():
         L.bsp_attn_fwd.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp]
         L.bsp_attn_fwd_varlen.argtypes = [P, ctypes.POINTER(BspVarlen), vp, vp, vp, vp, vp, vp,
                                           vp, vp]
+        L.bsp_score_varlen.argtypes = [P, ctypes.POINTER(BspVarlen), vp, vp, vp, vp, vp, vp]
+        L.bsp_mask_varlen.argtypes = [P, ctypes.POINTER(BspVarlen), vp, vp, vp, vp, vp, vp]
         f32 = ctypes.c_float
         L.bsp_calibrate_gamma.argtypes = [P, vp, f32, f32, vp, vp, vp, vp,
                                           ctypes.POINTER(f32), ctypes.POINTER(f32), vp]
         for f in (L.bsp_score, L.bsp_score_arith, L.bsp_score_rescue, L.bsp_mask,
                   L.bsp_mask_dual, L.bsp_attn_fwd, L.bsp_attn_fwd_varlen,
-                  L.bsp_calibrate_gamma):
+                  L.bsp_calibrate_gamma, L.bsp_score_varlen, L.bsp_mask_varlen):
             f.restype = ctypes.c_int32
         L.bsp_status_string.argtypes = [ctypes.c_int32]
         L.bsp_status_string.restype = ctypes.c_char_p
@@ -149,6 +152,18 @@ def bsp_attn_fwd_varlen(d: BspDesc, vl: BspVarlen, q, k_cache, v_cache, kv_idx, 
                         stream) -> int:
     return lib().bsp_attn_fwd_varlen(ctypes.byref(d), ctypes.byref(vl), q, k_cache, v_cache,
                                      kv_idx, kv_cnt, o, lse, stream)
+
+
+def bsp_score_varlen(d: BspDesc, vl: BspVarlen, q, k_cache, q_pool, k_pool, score_out,
+                     stream) -> int:
+    return lib().bsp_score_varlen(ctypes.byref(d), ctypes.byref(vl), q, k_cache, q_pool, k_pool,
+                                  score_out, stream)
+
+
+def bsp_mask_varlen(d: BspDesc, vl: BspVarlen, score_in, user_mask, mask_out, kv_idx, kv_cnt,
+                    stream) -> int:
+    return lib().bsp_mask_varlen(ctypes.byref(d), ctypes.byref(vl), score_in, user_mask, mask_out,
+                                 kv_idx, kv_cnt, stream)
 
 
 # ---------------------------------------------------------------- torch level
@@ -345,6 +360,91 @@ def attn_fwd(q, k, v, block: int, kv_idx=None, kv_cnt=None, sm_scale: float = 0.
     return o, lse
 
 
+def _varlen_meta(seqlens, block: int, ntok: int, device):
+    """Lengths, per-sequence block counts, total blocks and the device offset
+    arrays (cu_seqlens, cu_blocks) of a packed batch."""
+    lens = [int(x) for x in seqlens]
+    if not lens or min(lens) < 0:
+        raise BspError(2, "seqlens must be a non-empty list of lengths >= 0")
+    if ntok != sum(lens):
+        raise BspError(2, "the token axis must equal sum(seqlens)")
+    nbs = [-(-n // block) for n in lens]
+    cu_s = torch.tensor([0] + list(itertools.accumulate(lens)), dtype=torch.int32, device=device)
+    cu_b = torch.tensor([0] + list(itertools.accumulate(nbs)), dtype=torch.int32, device=device)
+    return lens, nbs, sum(nbs), cu_s, cu_b
+
+
+def _varlen_cache(q, k_cache, page_table, nbs, block: int):
+    d = q.shape[2]
+    if k_cache.dim() != 4 or k_cache.shape[2] != block or k_cache.shape[3] != d:
+        raise BspError(2, "k_cache must be [pages, hkv, block, d]")
+    if k_cache.dtype != q.dtype:
+        raise BspError(3, "q and the caches must share one dtype")
+    if (page_table.dim() != 2 or page_table.shape[0] != len(nbs)
+            or page_table.dtype != torch.int32):
+        raise BspError(2, "page_table must be int32 [nseq, max_pages]")
+    if page_table.shape[1] < max(nbs + [1]):
+        raise BspError(2, "page_table rows are shorter than a sequence's block count")
+
+
+def score_varlen(q, k_cache, page_table, seqlens, block: int, sm_scale: float = 0.0,
+                 q_scale=None, k_scale=None, idx_stride: Optional[int] = None):
+    """Stage 1 for a packed batch over a paged K cache (bsp_score_varlen).
+    Returns (q_pool [hq, total_blocks, d], k_pool [hkv, total_blocks, d],
+    score [hq, total_blocks, idx_stride]); idx_stride defaults to the largest
+    block count of a sequence.  Row entries past a sequence's block count are
+    left as allocated."""
+    hq, ntok, d = q.shape
+    lens, nbs, tb, cu_s, cu_b = _varlen_meta(seqlens, block, ntok, q.device)
+    _varlen_cache(q, k_cache, page_table, nbs, block)
+    hkv = k_cache.shape[1]
+    stride = max(nbs + [1]) if idx_stride is None else int(idx_stride)
+    if stride < max(nbs + [1]):
+        raise BspError(2, "idx_stride is smaller than a sequence's block count")
+    _shape(q_scale, (hq,), "q_scale")
+    _shape(k_scale, (hkv,), "k_scale")
+    dsc = desc(hq, hkv, ntok, d, block, _dtype_code(q), sm_scale=sm_scale, q_scale=q_scale,
+               k_scale=k_scale)
+    vl = BspVarlen(_ptr(cu_s), _ptr(cu_b), _ptr(page_table), len(lens), tb, page_table.shape[1],
+                   stride, None)
+    qp = torch.empty((hq, tb, d), dtype=torch.float32, device=q.device)
+    kp = torch.empty((hkv, tb, d), dtype=torch.float32, device=q.device)
+    sc = torch.empty((hq, tb, stride), dtype=torch.float32, device=q.device)
+    _check(bsp_score_varlen(dsc, vl, _ptr(q), _ptr(k_cache), _ptr(qp), _ptr(kp), _ptr(sc),
+                            _stream()))
+    return qp, kp, sc
+
+
+def mask_varlen(score_t: Optional[torch.Tensor], gamma: float, seqlens, block: int,
+                sink_blocks: int = 1, local_blocks: int = 1,
+                user_mask: Optional[torch.Tensor] = None, want_mask: bool = True):
+    """Stage 2 for a packed batch (bsp_mask_varlen).  score_t / user_mask:
+    [hq, total_blocks, idx_stride].  Returns (mask uint8 or None, kv_idx int32
+    [hq, total_blocks, idx_stride], kv_cnt int32 [hq, total_blocks]): the lists
+    bsp_attn_fwd_varlen reads."""
+    ref = score_t if score_t is not None else user_mask
+    hq, tb_in, stride = ref.shape
+    lens, nbs, tb, cu_s, cu_b = _varlen_meta(seqlens, block, sum(int(x) for x in seqlens),
+                                             ref.device)
+    if tb_in != tb or stride < max(nbs + [1]):
+        raise BspError(2, "score / user_mask do not match seqlens and block")
+    _shape(score_t, (hq, tb, stride), "score")
+    _shape(user_mask, (hq, tb, stride), "user_mask")
+    if score_t is not None and score_t.dtype != torch.float32:
+        raise BspError(3, "score must be float32")
+    if user_mask is not None and user_mask.dtype not in (torch.uint8, torch.bool):
+        raise BspError(3, "user_mask must be uint8")
+    dsc = desc(hq, 1, sum(lens), 64, block, DTYPE_F32, gamma=gamma, sink_blocks=sink_blocks,
+               local_blocks=local_blocks)
+    vl = BspVarlen(_ptr(cu_s), _ptr(cu_b), None, len(lens), tb, 1, stride, None)
+    m = torch.zeros((hq, tb, stride), dtype=torch.uint8, device=ref.device) if want_mask else None
+    idx = torch.empty((hq, tb, stride), dtype=torch.int32, device=ref.device)
+    cnt = torch.empty((hq, tb), dtype=torch.int32, device=ref.device)
+    _check(bsp_mask_varlen(dsc, vl, _ptr(score_t), _ptr(user_mask), _ptr(m), _ptr(idx),
+                           _ptr(cnt), _stream()))
+    return m, idx, cnt
+
+
 def attn_fwd_varlen(q, k_cache, v_cache, page_table, seqlens, block: int, kv_idx=None,
                     kv_cnt=None, sm_scale: float = 0.0, q_scale=None, k_scale=None,
                     v_scale=None, want_lse: bool = True, block_order=None):
@@ -354,28 +454,14 @@ def attn_fwd_varlen(q, k_cache, v_cache, page_table, seqlens, block: int, kv_idx
     kv_idx: int32 [hq, total_blocks, stride] with kv_cnt [hq, total_blocks];
     block_order: optional int32 [total_blocks] launch order of the blocks.
     Returns (o, lse) over the packed tokens."""
-    lens = [int(x) for x in seqlens]
-    if not lens or min(lens) < 0:
-        raise BspError(2, "seqlens must be a non-empty list of lengths >= 0")
     hq, ntok, d = q.shape
-    if ntok != sum(lens):
-        raise BspError(2, "q's token axis must equal sum(seqlens)")
-    if k_cache.dim() != 4 or k_cache.shape[2] != block or k_cache.shape[3] != d:
-        raise BspError(2, "k_cache must be [pages, hkv, block, d]")
+    lens, nbs, tb, cu_s, cu_b = _varlen_meta(seqlens, block, ntok, q.device)
+    nseq = len(lens)
+    _varlen_cache(q, k_cache, page_table, nbs, block)
     _shape(v_cache, k_cache.shape, "v_cache")
     hkv = k_cache.shape[1]
-    for t in (k_cache, v_cache):
-        if t.dtype != q.dtype:
-            raise BspError(3, "q and the caches must share one dtype")
-    nbs = [-(-n // block) for n in lens]
-    nseq = len(lens)
-    if page_table.dim() != 2 or page_table.shape[0] != nseq or page_table.dtype != torch.int32:
-        raise BspError(2, "page_table must be int32 [nseq, max_pages]")
-    if page_table.shape[1] < max(nbs + [1]):
-        raise BspError(2, "page_table rows are shorter than a sequence's block count")
-    tb = sum(nbs)
-    cu_s = torch.tensor([0] + list(itertools.accumulate(lens)), dtype=torch.int32, device=q.device)
-    cu_b = torch.tensor([0] + list(itertools.accumulate(nbs)), dtype=torch.int32, device=q.device)
+    if v_cache.dtype != q.dtype:
+        raise BspError(3, "q and the caches must share one dtype")
     stride = 1
     if kv_idx is not None:
         if kv_idx.dim() != 3 or kv_idx.shape[:2] != (hq, tb) or kv_idx.dtype != torch.int32:
@@ -400,6 +486,21 @@ def attn_fwd_varlen(q, k_cache, v_cache, page_table, seqlens, block: int, kv_idx
     _check(bsp_attn_fwd_varlen(dsc, vl, _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(kv_idx),
                                _ptr(kv_cnt), _ptr(o), _ptr(lse), _stream()))
     return o, lse
+
+
+def prefill_varlen(q, k_cache, v_cache, page_table, seqlens, block: int, gamma: float,
+                   sm_scale: float = 0.0, sink_blocks: int = 1, local_blocks: int = 1,
+                   q_scale=None, k_scale=None, v_scale=None):
+    """All three stages for a packed batch over a paged cache, on the current
+    stream.  Returns a dict of every output."""
+    out = {}
+    out["q_pool"], out["k_pool"], out["score"] = score_varlen(
+        q, k_cache, page_table, seqlens, block, sm_scale, q_scale, k_scale)
+    m, idx, cnt = mask_varlen(out["score"], gamma, seqlens, block, sink_blocks, local_blocks)
+    o, lse = attn_fwd_varlen(q, k_cache, v_cache, page_table, seqlens, block, idx, cnt, sm_scale,
+                             q_scale, k_scale, v_scale)
+    out.update(mask=m, kv_idx=idx, kv_cnt=cnt, o=o, lse=lse)
+    return out
 
 
 def prefill(q, k, v, block: int, gamma: float, sm_scale: float = 0.0, sink_blocks: int = 1,

@@ -91,11 +91,7 @@ __device__ __forceinline__ AttnRow attn_locate(int I, int seq, int nb, const Var
   if constexpr (VL) {
     // launch order: the caller's permutation (heaviest first), if given
     if (vl.block_order) r.gb = vl.block_order[nb - 1 - I];
-    int lo = 0, hi = vl.nseq;  // the sequence whose blocks contain gb
-    while (hi - lo > 1) {
-      const int mid = (lo + hi) >> 1;
-      if (vl.cu_blocks[mid] <= r.gb) lo = mid; else hi = mid;
-    }
+    const int lo = varlen_seq_of(vl.cu_blocks, vl.nseq, r.gb);
     r.I = r.gb - vl.cu_blocks[lo];
     r.tok0 = vl.cu_seqlens[lo];
     r.len = vl.cu_seqlens[lo + 1] - r.tok0;

@@ -251,6 +251,64 @@ bsp_status bsp_attn_fwd_varlen(const bsp_desc *desc, const bsp_varlen *vl, const
   return hip_status(bsp::launch_attn_varlen(s, a, v, (hipStream_t)stream));
 }
 
+// Shared checks of the packed-batch entry points; BSP_OK with *empty set
+// when there is nothing to do.
+static bsp_status check_varlen(const bsp_desc *desc, const bsp_varlen *vl, bool *empty) {
+  if (!vl) return BSP_ERR_NULL_POINTER;
+  if (vl->nseq < 1 || vl->total_blocks < 0 || vl->max_pages < 1 || vl->idx_stride < 1)
+    return BSP_ERR_BAD_SHAPE;
+  if ((long)desc->hq * vl->total_blocks > 0x7fffffffL ||
+      (long)desc->hq * vl->total_blocks * vl->idx_stride > 0x7fffffffffffL)
+    return BSP_ERR_BAD_SHAPE;
+  *empty = desc->seq == 0 || vl->total_blocks == 0;
+  if (!*empty && (!vl->cu_seqlens || !vl->cu_blocks)) return BSP_ERR_NULL_POINTER;
+  return BSP_OK;
+}
+
+bsp_status bsp_score_varlen(const bsp_desc *desc, const bsp_varlen *vl, const void *q,
+                            const void *k_cache, float *q_pool, float *k_pool, float *score,
+                            void *stream) {
+  bsp_status st = check_desc(desc, true);
+  if (st != BSP_OK) return st;
+  bool empty = false;
+  if ((st = check_varlen(desc, vl, &empty)) != BSP_OK) return st;
+  if (empty) return BSP_OK;
+  if (!vl->page_table || !q || !k_cache || !q_pool || !k_pool || !score)
+    return BSP_ERR_NULL_POINTER;
+  const bool fp8 = desc->dtype == BSP_DTYPE_FP8_E4M3;
+  if (fp8 && (!desc->q_scale || !desc->k_scale)) return BSP_ERR_BAD_DTYPE;
+  if (!fp8 && (desc->q_scale || desc->k_scale || desc->v_scale)) return BSP_ERR_BAD_DTYPE;
+  Shape s = shape_of(desc);
+  s.nb = vl->total_blocks;
+  const bsp::VarlenArgs v{vl->cu_seqlens, vl->cu_blocks, vl->page_table, vl->block_order,
+                          vl->nseq,       vl->max_pages, vl->idx_stride};
+  hipStream_t hs = (hipStream_t)stream;
+  if (bsp::launch_pool_varlen(s, v, q, k_cache, desc->q_scale, desc->k_scale, q_pool, k_pool,
+                              hs) != hipSuccess)
+    return BSP_ERR_HIP;
+  return hip_status(bsp::launch_score_varlen(s, v, scale_of(desc), q_pool, k_pool, score, hs));
+}
+
+bsp_status bsp_mask_varlen(const bsp_desc *desc, const bsp_varlen *vl, const float *score,
+                           const uint8_t *user_mask, uint8_t *mask, int32_t *kv_idx,
+                           int32_t *kv_cnt, void *stream) {
+  bsp_status st = check_desc(desc, false);
+  if (st != BSP_OK) return st;
+  if (!(desc->gamma >= 0.f && desc->gamma <= 1.f)) return BSP_ERR_BAD_VALUE;  // also NaN
+  if (desc->sink_blocks < 0 || desc->local_blocks < 0) return BSP_ERR_BAD_VALUE;
+  bool empty = false;
+  if ((st = check_varlen(desc, vl, &empty)) != BSP_OK) return st;
+  if (empty) return BSP_OK;
+  if ((!score && !user_mask) || !kv_idx || !kv_cnt) return BSP_ERR_NULL_POINTER;
+  Shape s = shape_of(desc);
+  s.nb = vl->total_blocks;
+  const bsp::VarlenArgs v{vl->cu_seqlens, vl->cu_blocks, vl->page_table, vl->block_order,
+                          vl->nseq,       vl->max_pages, vl->idx_stride};
+  return hip_status(bsp::launch_mask_varlen(s, v, desc->gamma, desc->sink_blocks,
+                                            desc->local_blocks, score, user_mask, mask, kv_idx,
+                                            kv_cnt, (hipStream_t)stream));
+}
+
 const char *bsp_status_string(int32_t status) {
   switch (status) {
     case BSP_OK: return "BSP_OK";

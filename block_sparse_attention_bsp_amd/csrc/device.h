@@ -61,6 +61,18 @@ __device__ __forceinline__ uint32_t f32_to_bf16_bits(float x) {
   return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
 }
 
+// Packed variable-length batch: the sequence whose query blocks
+// cu_blocks[s] .. cu_blocks[s+1] contain batch block gb (binary search over
+// the nseq + 1 nondecreasing offsets).
+__device__ __forceinline__ int varlen_seq_of(const int32_t *cu_blocks, int nseq, int gb) {
+  int lo = 0, hi = nseq;
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if (cu_blocks[mid] <= gb) lo = mid; else hi = mid;
+  }
+  return lo;
+}
+
 __device__ __forceinline__ float wave_max(float v) {
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));

@@ -39,6 +39,18 @@ struct VarlenArgs {
   int nseq, max_pages, idx_stride;
 };
 
+// Packed variable-length batches (s.seq = the batch's tokens, s.nb = its
+// query blocks): stage 1 over Q and the paged K cache, per-sequence block
+// scores in rows of stride vl.idx_stride, and the mask with the same rows.
+hipError_t launch_pool_varlen(const Shape &s, const VarlenArgs &vl, const void *q,
+                              const void *k_cache, const float *q_scale, const float *k_scale,
+                              float *q_pool, float *k_pool, hipStream_t st);
+hipError_t launch_score_varlen(const Shape &s, const VarlenArgs &vl, float c, const float *q_pool,
+                               const float *k_pool, float *score, hipStream_t st);
+hipError_t launch_mask_varlen(const Shape &s, const VarlenArgs &vl, float gamma, int sink,
+                              int local, const float *score, const uint8_t *user, uint8_t *mask,
+                              int32_t *kv_idx, int32_t *kv_cnt, hipStream_t st);
+
 hipError_t launch_attn_f32(const Shape &s, const AttnArgs &a, hipStream_t st);
 hipError_t launch_attn_varlen(const Shape &s, const AttnArgs &a, const VarlenArgs &v,
                               hipStream_t st);

@@ -21,7 +21,10 @@
 
 namespace bsp {
 
-template <bool DUAL>
+// VL: rows of a packed variable-length batch: row h * nb + gb (nb = the
+// batch's query blocks) belongs to sequence s and is its query block
+// I = gb - cu_blocks[s]; it has the sequence's nb_s columns and stride ld.
+template <bool DUAL, bool VL>
 __global__ __launch_bounds__(256) void mask_kernel(const float *__restrict__ P,
                                                    const float *__restrict__ Pr,
                                                    const uint8_t *__restrict__ user,
@@ -29,21 +32,29 @@ __global__ __launch_bounds__(256) void mask_kernel(const float *__restrict__ P,
                                                    int32_t *__restrict__ kv_idx,
                                                    int32_t *__restrict__ kv_cnt, int rows, int nb,
                                                    float gamma, float gamma_r, int sink,
-                                                   int local) {
+                                                   int local, int ld, VarlenArgs vl) {
   const int lane = threadIdx.x & 63;
   const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (row >= rows) return;
-  const int I = row % nb;
-  const size_t off = (size_t)row * nb;
-  const bool vec = (nb & 3) == 0;  // rows are 16-byte aligned
+  int I = row % nb, ncol = nb;
+  if constexpr (VL) {
+    const int sq = varlen_seq_of(vl.cu_blocks, vl.nseq, I);
+    // a row never reaches past its stride, whatever the offsets say
+    ncol = min(vl.cu_blocks[sq + 1] - vl.cu_blocks[sq], ld);
+    I = min(I - vl.cu_blocks[sq], ncol - 1);
+  } else {
+    ld = nb;
+  }
+  const size_t off = (size_t)row * ld;
+  const bool vec = (ld & 3) == 0;  // rows are 16-byte aligned
 
   auto load4 = [&](const float *p, int J, float (&x)[4]) {
-    if (vec && J + 3 < nb) {
+    if (vec && J + 3 < ncol) {
       const float4 t = *(const float4 *)(p + J);
       x[0] = t.x; x[1] = t.y; x[2] = t.z; x[3] = t.w;
     } else {
 #pragma unroll
-      for (int e = 0; e < 4; ++e) x[e] = J + e < nb ? p[J + e] : 0.f;
+      for (int e = 0; e < 4; ++e) x[e] = J + e < ncol ? p[J + e] : 0.f;
     }
   };
 
@@ -67,18 +78,18 @@ __global__ __launch_bounds__(256) void mask_kernel(const float *__restrict__ P,
 
   const uint64_t below = (1ull << lane) - 1ull;
   int n = 0;
-  for (int J0 = 0; J0 < nb; J0 += 256) {
+  for (int J0 = 0; J0 < ncol; J0 += 256) {
     const int J = J0 + 4 * lane;
     bool keep[4] = {false, false, false, false};
     if (J <= I) {
       if (user) {
-        if (vec && J + 3 < nb) {
+        if (vec && J + 3 < ncol) {
           const uint32_t u4 = *(const uint32_t *)(user + off + J);
 #pragma unroll
           for (int e = 0; e < 4; ++e) keep[e] = ((u4 >> (8 * e)) & 0xFFu) != 0;
         } else {
 #pragma unroll
-          for (int e = 0; e < 4; ++e) keep[e] = J + e < nb && user[off + J + e] != 0;
+          for (int e = 0; e < 4; ++e) keep[e] = J + e < ncol && user[off + J + e] != 0;
         }
       } else {
         float x[4], y[4];
@@ -94,13 +105,13 @@ __global__ __launch_bounds__(256) void mask_kernel(const float *__restrict__ P,
       for (int e = 0; e < 4; ++e) keep[e] = keep[e] && J + e <= I;
     }
     if (mask) {
-      if (vec && J + 3 < nb) {
+      if (vec && J + 3 < ncol) {
         *(uint32_t *)(mask + off + J) = (uint32_t)keep[0] | ((uint32_t)keep[1] << 8) |
                                         ((uint32_t)keep[2] << 16) | ((uint32_t)keep[3] << 24);
       } else {
 #pragma unroll
         for (int e = 0; e < 4; ++e)
-          if (J + e < nb) mask[off + J + e] = keep[e] ? 1 : 0;
+          if (J + e < ncol) mask[off + J + e] = keep[e] ? 1 : 0;
       }
     }
     uint64_t bal[4];
@@ -230,8 +241,8 @@ static hipError_t launch_mask_t(const Shape &s, float gamma, float gamma_r, int 
   else if (!user && s.nb <= 2048)
     BSP_MASK_REG(8);
   else
-    hipLaunchKernelGGL((mask_kernel<DUAL>), grid, block, 0, st, score, rescue, user, mask, idx,
-                       cnt, rows, s.nb, gamma, gamma_r, sink, local);
+    hipLaunchKernelGGL((mask_kernel<DUAL, false>), grid, block, 0, st, score, rescue, user, mask,
+                       idx, cnt, rows, s.nb, gamma, gamma_r, sink, local, s.nb, VarlenArgs{});
 #undef BSP_MASK_REG
   return hipGetLastError();
 }
@@ -243,6 +254,16 @@ hipError_t launch_mask(const Shape &s, float gamma, int sink, int local, const f
     return launch_mask_t<true>(s, gamma, gamma_r, sink, local, score, rescue, nullptr, mask, idx,
                                cnt, st);
   return launch_mask_t<false>(s, gamma, 0.f, sink, local, score, nullptr, user, mask, idx, cnt, st);
+}
+
+hipError_t launch_mask_varlen(const Shape &s, const VarlenArgs &vl, float gamma, int sink,
+                              int local, const float *score, const uint8_t *user, uint8_t *mask,
+                              int32_t *idx, int32_t *cnt, hipStream_t st) {
+  const int rows = s.hq * s.nb;
+  hipLaunchKernelGGL((mask_kernel<false, true>), dim3((rows + 3) / 4), dim3(256), 0, st,
+                     user ? nullptr : score, nullptr, user, mask, idx, cnt, rows, s.nb, gamma, 0.f,
+                     sink, local, vl.idx_stride, vl);
+  return hipGetLastError();
 }
 
 }  // namespace bsp

@@ -17,14 +17,18 @@ namespace bsp {
 
 typedef unsigned int u32x4v __attribute__((ext_vector_type(4)));
 
-template <int DT, int D, int BLK>
+// VL: a packed variable-length batch (seq = its tokens, nb = its query
+// blocks); the query block of batch block I is block I - cu_blocks[s] of
+// sequence s, and its keys are cache page page_table[s][that block], laid out
+// [page][hkv][BLK][d].
+template <int DT, int D, int BLK, bool VL>
 __global__ __launch_bounds__(256) void pool_kernel(const uint8_t *__restrict__ q,
                                                    const uint8_t *__restrict__ k,
                                                    const float *__restrict__ q_scale,
                                                    const float *__restrict__ k_scale,
                                                    float *__restrict__ q_pool,
-                                                   float *__restrict__ k_pool, int hq, int seq,
-                                                   int nb, int nslab) {
+                                                   float *__restrict__ k_pool, int hq, int hkv,
+                                                   int seq, int nb, int nslab, VarlenArgs vl) {
   constexpr int ES = Storage<DT>::bytes;
   constexpr int VEC = 16 / ES;     // elements per 16-byte chunk
   constexpr int CH = D / VEC;      // chunks per row (4..32)
@@ -37,9 +41,19 @@ __global__ __launch_bounds__(256) void pool_kernel(const uint8_t *__restrict__ q
   const int hh = sl / nb, I = sl - hh * nb;
   const bool isq = hh < hq;
   const int h = isq ? hh : hh - hq;
-  const int t0 = I * BLK;
-  const int rows = min(BLK, seq - t0);
-  const uint8_t *base = (isq ? q : k) + ((size_t)h * seq + t0) * D * ES;
+  int rows;
+  const uint8_t *base;
+  if constexpr (VL) {
+    const int sq = varlen_seq_of(vl.cu_blocks, vl.nseq, I);
+    const int Il = I - vl.cu_blocks[sq], tok0 = vl.cu_seqlens[sq];
+    rows = min(BLK, vl.cu_seqlens[sq + 1] - tok0 - Il * BLK);
+    base = isq ? q + ((size_t)h * seq + tok0 + Il * BLK) * D * ES
+               : k + ((size_t)vl.page_table[(size_t)sq * vl.max_pages + Il] * hkv + h) * BLK * D * ES;
+  } else {
+    const int t0 = I * BLK;
+    rows = min(BLK, seq - t0);
+    base = (isq ? q : k) + ((size_t)h * seq + t0) * D * ES;
+  }
   const int c = lane % CH, r0 = lane / CH;
 
   float acc[VEC];
@@ -92,30 +106,48 @@ __global__ __launch_bounds__(256) void pool_kernel(const uint8_t *__restrict__ q
   }
 }
 
-template <int DT, int D, int BLK>
+template <int DT, int D, int BLK, bool VL>
 static hipError_t launch_pool_t(const Shape &s, const void *q, const void *k, const float *qs,
-                                const float *ks, float *qp, float *kp, hipStream_t st) {
+                                const float *ks, float *qp, float *kp, const VarlenArgs &vl,
+                                hipStream_t st) {
   const int nslab = (s.hq + s.hkv) * s.nb;
-  hipLaunchKernelGGL((pool_kernel<DT, D, BLK>), dim3((nslab + 3) / 4), dim3(256), 0, st,
-                     (const uint8_t *)q, (const uint8_t *)k, qs, ks, qp, kp, s.hq, s.seq, s.nb,
-                     nslab);
+  hipLaunchKernelGGL((pool_kernel<DT, D, BLK, VL>), dim3((nslab + 3) / 4), dim3(256), 0, st,
+                     (const uint8_t *)q, (const uint8_t *)k, qs, ks, qp, kp, s.hq, s.hkv, s.seq,
+                     s.nb, nslab, vl);
   return hipGetLastError();
 }
 
-template <int DT>
+template <int DT, bool VL>
 static hipError_t launch_pool_dt(const Shape &s, const void *q, const void *k, const float *qs,
-                                 const float *ks, float *qp, float *kp, hipStream_t st) {
-  if (s.d == 64 && s.block == 64) return launch_pool_t<DT, 64, 64>(s, q, k, qs, ks, qp, kp, st);
-  if (s.d == 64 && s.block == 128) return launch_pool_t<DT, 64, 128>(s, q, k, qs, ks, qp, kp, st);
-  if (s.d == 128 && s.block == 64) return launch_pool_t<DT, 128, 64>(s, q, k, qs, ks, qp, kp, st);
-  return launch_pool_t<DT, 128, 128>(s, q, k, qs, ks, qp, kp, st);
+                                 const float *ks, float *qp, float *kp, const VarlenArgs &vl,
+                                 hipStream_t st) {
+  if (s.d == 64 && s.block == 64)
+    return launch_pool_t<DT, 64, 64, VL>(s, q, k, qs, ks, qp, kp, vl, st);
+  if (s.d == 64 && s.block == 128)
+    return launch_pool_t<DT, 64, 128, VL>(s, q, k, qs, ks, qp, kp, vl, st);
+  if (s.d == 128 && s.block == 64)
+    return launch_pool_t<DT, 128, 64, VL>(s, q, k, qs, ks, qp, kp, vl, st);
+  return launch_pool_t<DT, 128, 128, VL>(s, q, k, qs, ks, qp, kp, vl, st);
+}
+
+template <bool VL>
+static hipError_t launch_pool_any(const Shape &s, const void *q, const void *k, const float *qs,
+                                  const float *ks, float *qp, float *kp, const VarlenArgs &vl,
+                                  hipStream_t st) {
+  if (s.dtype == kF32) return launch_pool_dt<kF32, VL>(s, q, k, qs, ks, qp, kp, vl, st);
+  if (s.dtype == kBF16) return launch_pool_dt<kBF16, VL>(s, q, k, qs, ks, qp, kp, vl, st);
+  return launch_pool_dt<kFP8, VL>(s, q, k, qs, ks, qp, kp, vl, st);
 }
 
 hipError_t launch_pool(const Shape &s, const void *q, const void *k, const float *qs,
                        const float *ks, float *qp, float *kp, hipStream_t st) {
-  if (s.dtype == kF32) return launch_pool_dt<kF32>(s, q, k, qs, ks, qp, kp, st);
-  if (s.dtype == kBF16) return launch_pool_dt<kBF16>(s, q, k, qs, ks, qp, kp, st);
-  return launch_pool_dt<kFP8>(s, q, k, qs, ks, qp, kp, st);
+  return launch_pool_any<false>(s, q, k, qs, ks, qp, kp, VarlenArgs{}, st);
+}
+
+hipError_t launch_pool_varlen(const Shape &s, const VarlenArgs &vl, const void *q,
+                              const void *k_cache, const float *qs, const float *ks, float *qp,
+                              float *kp, hipStream_t st) {
+  return launch_pool_any<true>(s, q, k_cache, qs, ks, qp, kp, vl, st);
 }
 
 }  // namespace bsp

@@ -441,6 +441,68 @@ static hipError_t launch_score_t(const Shape &s, float c, const float *qp, const
   return hipGetLastError();
 }
 
+// Packed variable-length batch: one wavefront per (q head, batch block gb)
+// row, lane j taking the key blocks j, j + 64, ... of the row's own
+// sequence.  Each score is an fp32 dot product of the (wave-uniform, hence
+// scalar-loaded) Qbar row with the lane's Kbar row; a sequence has few
+// blocks, so these rows are too short to fill matrix-core tiles.  Pass 1
+// writes the log2-domain scores and keeps a per-lane running max and sum;
+// after the wave combines them, pass 2 rewrites the row normalised.  Row gb
+// has stride ld; its entries J < nb_s are written (0 for J > I).
+template <int D>
+__global__ __launch_bounds__(256) void score_vl_kernel(const float *__restrict__ q_pool,
+                                                       const float *__restrict__ k_pool,
+                                                       float *__restrict__ P, int hq, int hkv,
+                                                       int nb, int ld, VarlenArgs vl, float c2) {
+  const int lane = threadIdx.x & 63;
+  const int row = __builtin_amdgcn_readfirstlane(blockIdx.x * 4 + (threadIdx.x >> 6));
+  if (row >= hq * nb) return;
+  const int h = row / nb, gb = row - h * nb;
+  const int g = h / (hq / hkv);
+  const int sq = varlen_seq_of(vl.cu_blocks, vl.nseq, gb);
+  // a row never writes past its stride, whatever the offsets say
+  const int cb0 = vl.cu_blocks[sq], ncol = min(vl.cu_blocks[sq + 1] - cb0, ld);
+  const int I = min(gb - cb0, ncol - 1);
+  const float *qrow = q_pool + (size_t)row * D;
+  const float *kbase = k_pool + ((size_t)g * nb + cb0) * D;
+  float *prow = P + (size_t)row * ld;
+
+  float m = -INFINITY, l = 0.f;
+  for (int J = lane; J <= I; J += 64) {
+    const float *krow = kbase + (size_t)J * D;
+    float a0 = 0.f, a1 = 0.f;
+#pragma unroll
+    for (int i = 0; i < D; i += 8) {
+      const float4 k0 = *(const float4 *)(krow + i), k1 = *(const float4 *)(krow + i + 4);
+      const float4 q0 = *(const float4 *)(qrow + i), q1 = *(const float4 *)(qrow + i + 4);
+      a0 = fmaf(q0.x, k0.x, fmaf(q0.y, k0.y, fmaf(q0.z, k0.z, fmaf(q0.w, k0.w, a0))));
+      a1 = fmaf(q1.x, k1.x, fmaf(q1.y, k1.y, fmaf(q1.z, k1.z, fmaf(q1.w, k1.w, a1))));
+    }
+    const float x = (a0 + a1) * c2;
+    prow[J] = x;
+    const float mn = fmaxf(m, x);
+    l = l * exp2f(m - mn) + exp2f(x - mn);
+    m = mn;
+  }
+  const float M = wave_max(m);
+  float L = m == -INFINITY ? 0.f : l * exp2f(m - M);
+  L = wave_sum(L);
+  const float inv = L > 0.f ? 1.f / L : 0.f;
+  for (int J = lane; J < ncol; J += 64) prow[J] = J <= I ? exp2f(prow[J] - M) * inv : 0.f;
+}
+
+hipError_t launch_score_varlen(const Shape &s, const VarlenArgs &vl, float c, const float *q_pool,
+                               const float *k_pool, float *S, hipStream_t st) {
+  const int rows = s.hq * s.nb;
+  if (s.d == 64)
+    hipLaunchKernelGGL((score_vl_kernel<64>), dim3((rows + 3) / 4), dim3(256), 0, st, q_pool,
+                       k_pool, S, s.hq, s.hkv, s.nb, vl.idx_stride, vl, c * kLog2e);
+  else
+    hipLaunchKernelGGL((score_vl_kernel<128>), dim3((rows + 3) / 4), dim3(256), 0, st, q_pool,
+                       k_pool, S, s.hq, s.hkv, s.nb, vl.idx_stride, vl, c * kLog2e);
+  return hipGetLastError();
+}
+
 hipError_t launch_score(const Shape &s, float c, const float *q_pool, const float *k_pool,
                         const float *k_radius, float *S, hipStream_t st) {
   if (k_radius) {

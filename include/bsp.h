@@ -44,7 +44,7 @@
 extern "C" {
 #endif
 
-#define BSP_ABI_VERSION 5
+#define BSP_ABI_VERSION 6
 
 typedef enum bsp_status {
   BSP_OK = 0,
@@ -282,6 +282,54 @@ typedef struct {
 bsp_status bsp_attn_fwd_varlen(const bsp_desc *desc, const bsp_varlen *vl, const void *q,
                                const void *k_cache, const void *v_cache, const int32_t *kv_idx,
                                const int32_t *kv_cnt, void *o, float *lse, void *stream);
+
+/*
+ * bsp_score_varlen - bsp_score for a packed batch over a paged K cache
+ * (FlashPrefill V2 abstract: paged KV cache and continuous batching; the
+ * stage itself as for bsp_score).  Per sequence s, exactly bsp_score on its
+ * own tokens; the block means of all sequences are laid out in batch block
+ * order and each sequence's score matrix occupies rows
+ * cu_blocks[s] .. cu_blocks[s+1] of a [hq][total_blocks][idx_stride] array:
+ *   q_pool[h][gb][:] = mean of Q[h][t][:] over the tokens t of batch block gb
+ *   k_pool[g][gb][:] = mean of the valid rows of cache page page_table[s][I]
+ *   score[h][gb][J]  = the row softmax of c * q_pool[h][gb] . k_pool[g][cb + J]
+ *                      over J <= I, 0 for I < J < nb_s
+ * with gb = cb + I, cb = cu_blocks[s], nb_s = cu_blocks[s+1] - cb.  Entries
+ * J >= nb_s of a row are not written.  The scores are fp32 dot products.
+ *
+ * q:        device [hq][desc->seq][d], storage dtype (desc->seq = tokens in the batch)
+ * k_cache:  device [pages][hkv][block][d], storage dtype
+ * q_pool:   device float [hq][total_blocks][d]   (written)
+ * k_pool:   device float [hkv][total_blocks][d]  (written)
+ * score:    device float [hq][total_blocks][idx_stride] (written as above)
+ * vl:       as for bsp_attn_fwd_varlen (block_order is not read);
+ *           idx_stride >= the largest nb_s
+ * Needs desc->q_scale and desc->k_scale for fp8 (v_scale is not read).
+ */
+bsp_status bsp_score_varlen(const bsp_desc *desc, const bsp_varlen *vl, const void *q,
+                            const void *k_cache, float *q_pool, float *k_pool, float *score,
+                            void *stream);
+
+/*
+ * bsp_mask_varlen - bsp_mask for a packed batch: per sequence, exactly
+ * bsp_mask on its rows (the threshold against its own row maximum, sink and
+ * local window counted from its own first block), with rows gb =
+ * cu_blocks[s] + I of stride idx_stride.  The lists it writes are what
+ * bsp_attn_fwd_varlen reads: block indices local to the sequence.
+ *
+ * score:     device float [hq][total_blocks][idx_stride] from bsp_score_varlen;
+ *            may be NULL iff user_mask is given
+ * user_mask: device uint8 [hq][total_blocks][idx_stride] or NULL (replaces the
+ *            threshold and the forced blocks, ANDed with causal)
+ * mask:      device uint8 [hq][total_blocks][idx_stride] or NULL; entries
+ *            J < nb_s of each row are written
+ * kv_idx:    device int32 [hq][total_blocks][idx_stride]; first kv_cnt entries
+ * kv_cnt:    device int32 [hq][total_blocks]
+ * vl:        cu_seqlens, cu_blocks, nseq, total_blocks, idx_stride are read
+ */
+bsp_status bsp_mask_varlen(const bsp_desc *desc, const bsp_varlen *vl, const float *score,
+                           const uint8_t *user_mask, uint8_t *mask, int32_t *kv_idx,
+                           int32_t *kv_cnt, void *stream);
 
 /* Static description of a status code (host, never NULL). */
 const char *bsp_status_string(int32_t status);

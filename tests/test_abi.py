@@ -28,8 +28,9 @@ def built():
 
 def test_header_declares_the_entry_points():
     assert _declared() == ["bsp_abi_version", "bsp_attn_fwd", "bsp_attn_fwd_varlen",
-                           "bsp_calibrate_gamma", "bsp_mask", "bsp_mask_dual", "bsp_score",
-                           "bsp_score_arith", "bsp_score_rescue", "bsp_status_string"]
+                           "bsp_calibrate_gamma", "bsp_mask", "bsp_mask_dual", "bsp_mask_varlen",
+                           "bsp_score", "bsp_score_arith", "bsp_score_rescue",
+                           "bsp_score_varlen", "bsp_status_string"]
 
 
 def test_library_exports_every_declared_symbol():
@@ -174,3 +175,32 @@ def test_varlen_host_checks():
     assert bsp.lib().bsp_attn_fwd_varlen(ctypes.byref(d), None, fake, fake, fake, None, None,
                                          fake, None, None) == 1
     assert ctypes.sizeof(bsp.BspVarlen) == 3 * 8 + 4 * 4 + 8
+
+
+def test_varlen_score_and_mask_host_checks():
+    fake = 0x1000  # never dereferenced: every case fails before a launch
+    d = bsp.desc(4, 1, 1024, 64, 64, bsp.DTYPE_BF16, gamma=0.1)
+    ok = dict(cu_seqlens=fake, cu_blocks=fake, page_table=fake, nseq=2, total_blocks=16,
+              max_pages=16, idx_stride=16)
+    vl = lambda **kw: bsp.BspVarlen(**{**ok, **kw})
+    score = lambda dd, v, **kw: bsp.bsp_score_varlen(dd, v, kw.get("q", fake), fake, fake, fake,
+                                                     kw.get("s", fake), None)
+    mask = lambda dd, v, **kw: bsp.bsp_mask_varlen(dd, v, kw.get("s", fake), None, None,
+                                                   kw.get("i", fake), fake, None)
+    for fn in (score, mask):
+        assert fn(d, vl(nseq=0)) == 2
+        assert fn(d, vl(total_blocks=-1)) == 2
+        assert fn(d, vl(idx_stride=0)) == 2
+        assert fn(d, vl(cu_blocks=None)) == 1
+        assert fn(d, vl(total_blocks=0)) == 0  # nothing to do
+        assert fn(bsp.desc(4, 3, 1024, 64, 64, bsp.DTYPE_BF16), vl()) == 2  # hq % hkv
+    assert score(d, vl(page_table=None)) == 1
+    assert score(d, vl(), q=None) == 1
+    assert score(d, vl(), s=None) == 1
+    d8 = bsp.desc(4, 1, 1024, 64, 64, bsp.DTYPE_FP8_E4M3)
+    assert score(d8, vl()) == 3  # fp8 needs q_scale and k_scale
+    assert mask(d, vl(), s=None) == 1  # neither scores nor a caller mask
+    assert mask(d, vl(), i=None) == 1
+    assert mask(bsp.desc(4, 1, 1024, 64, 64, bsp.DTYPE_BF16, gamma=1.5), vl()) == 4
+    assert bsp.lib().bsp_score_varlen(ctypes.byref(d), None, fake, fake, fake, fake, fake,
+                                      None) == 1

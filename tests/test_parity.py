@@ -304,6 +304,66 @@ def test_varlen_paged_matches_oracle_per_sequence(dtype, d, block, dense):
     print(f"  max-abs O err {err:.2e}", flush=True)
 
 
+@pytest.mark.parametrize("dtype,d,block,gamma", [("bf16", 128, 128, 0.3), ("fp8", 128, 128, 0.2),
+                                                  ("bf16", 64, 64, 0.4), ("fp8", 64, 64, 0.3)])
+def test_varlen_pipeline_matches_oracle_per_sequence(dtype, d, block, gamma):
+    """Score, mask and attention of a packed batch over a shuffled paged cache
+    (unused cache rows NaN bits): every sequence against the oracle run on
+    that sequence alone."""
+    import dataclasses
+    lens = [1000, 130, 512, 64, 777, 1, 900]
+    announce(f"varlen pipeline {dtype} d={d} B={block} gamma={gamma} lens={lens}")
+    c = gen.make_case(4, 2, sum(lens), d, block, dtype, 47 + d, rope=True, n_vert=4,
+                      block_offset=1.5)  # masks keep 45-73% of the causal blocks
+    rng = np.random.default_rng(d + block)
+    nbs = [-(-n // block) for n in lens]
+    tb = sum(nbs)
+    npages = tb + 5
+    perm = rng.permutation(npages).astype(np.int32)
+    kc = np.full((npages, c.hkv, block, d), _NAN_BITS[dtype], c.k.dtype)
+    vc = np.full_like(kc, _NAN_BITS[dtype])
+    ptab = np.zeros((len(lens), max(nbs) + 1), np.int32)
+    t0, b0 = 0, 0
+    for s_, (n, nb) in enumerate(zip(lens, nbs)):
+        for J in range(nb):
+            pg = perm[b0 + J]
+            ptab[s_, J] = pg
+            r1 = min(block, n - J * block)
+            kc[pg, :, :r1] = c.k[:, t0 + J * block:t0 + J * block + r1]
+            vc[pg, :, :r1] = c.v[:, t0 + J * block:t0 + J * block + r1]
+        t0 += n
+        b0 += nb
+    dv = H.dev(c)
+    t = lambda x: (torch.from_numpy(x.view(np.int16)).cuda().view(torch.bfloat16) if dtype == "bf16"
+                   else torch.from_numpy(x).cuda())
+    res = bsp.prefill_varlen(dv["q"], t(kc), t(vc), torch.from_numpy(ptab).cuda(), lens, block,
+                             gamma, q_scale=dv["q_scale"], k_scale=dv["k_scale"],
+                             v_scale=dv["v_scale"])
+    torch.cuda.synchronize()
+    g = {k_: v_.cpu().numpy() for k_, v_ in res.items() if v_ is not None and k_ not in ("o", "lse")}
+    go, gl = res["o"].float().cpu().numpy(), res["lse"].cpu().numpy()
+    t0, cb, err, nband = 0, 0, 0.0, 0
+    for n, nb in zip(lens, nbs):
+        sub = dataclasses.replace(c, seq=n, q=c.q[:, t0:t0 + n], k=c.k[:, t0:t0 + n],
+                                  v=c.v[:, t0:t0 + n])
+        orc = oracle.prefill(sub, gamma, with_attn=False)
+        rb = slice(cb, cb + nb)
+        np.testing.assert_allclose(g["q_pool"][:, rb], orc["qbar"], rtol=1e-5, atol=2e-6)
+        np.testing.assert_allclose(g["k_pool"][:, rb], orc["kbar"], rtol=1e-5, atol=2e-6)
+        np.testing.assert_allclose(g["score"][:, rb, :nb], orc["P"], rtol=1e-4, atol=1e-6)
+        gm = g["mask"][:, rb, :nb]
+        nband += H.check_mask(gm, g["kv_idx"][:, rb, :nb], g["kv_cnt"][:, rb], orc, gamma)
+        oo, ol = oracle.attn(sub.q, sub.k, sub.v, dtype, block, gm, q_scale=c.q_scale,
+                             k_scale=c.k_scale, v_scale=c.v_scale)
+        sl = slice(t0, t0 + n)
+        err = max(err, H.check_attn(go[:, sl].reshape(-1, d), gl[:, sl].reshape(-1),
+                                    oo.reshape(-1, d), ol.reshape(-1), dtype))
+        t0 += n
+        cb += nb
+    dens = g["mask"].sum() / sum(c.hq * nb * (nb + 1) / 2 for nb in nbs)
+    print(f"  density {dens:.3f} band {nband} max-abs O err {err:.2e}", flush=True)
+
+
 @pytest.mark.parametrize("which,target", [("s1_0", 0.3), ("s1_1", 0.7), ("llama_4k", 0.7)])
 def test_calibrate_gamma_matches_oracle(which, target):
     """Bisection on the GPU masks lands on the oracle's gamma; the buffers
