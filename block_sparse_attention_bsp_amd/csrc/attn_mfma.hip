@@ -85,15 +85,17 @@ __device__ __forceinline__ int k_unit(int r, int u) {
   return u ^ ((r / C::KRPW) % C::UNITS);
 }
 
-// V rows are split into 64-byte groups; the group index is XORed with the
-// row so the four rows a ds_read_b64_tr_b16 lane group touches hit distinct
-// banks, while a 64-byte group stays contiguous.  Invariant under +4 rows
-// (d = 128) / +8 rows (d = 64), so per-lane offsets are loop constants.
+// V rows are stored in 16-byte chunks whose index is XORed with a function
+// of the row that moves whole 32-byte pairs, so that the rows one
+// ds_read_b64_tr_b16 reads together (32 bytes from each of 4 rows per 16
+// lanes, 8 rows per 32 lanes) land on distinct banks: 128 B per 16 lanes
+// and 256 B per 32 lanes, no bank taken twice (measured with the LDS
+// bank-conflict counter).  Depends on the row modulo 8 only, so per-lane
+// offsets are loop constants.
 template <int D>
 __device__ __forceinline__ int v_chunk(int r, int c) {
-  constexpr int VRPW = D >= 128 ? 1 : 128 / D;  // rows per 256-byte window
-  constexpr int NG = D / 32;                     // 64-byte groups per row
-  return c ^ (((r / VRPW) % NG) << 2);
+  if constexpr (D >= 128) return c ^ ((r & 7) << 1);
+  return c ^ ((((r ^ (r >> 2)) & 1) << 1) | (((r >> 1) & 1) << 2));
 }
 
 
@@ -123,7 +125,7 @@ struct Attn {
   // per-lane byte offsets (loop constants)
   uint32_t kdma[KPW / 64], vdma[DT == kBF16 ? VPW / 64 : 1];
   int krow[KPW / 64], vrow[DT == kBF16 ? VPW / 64 : 1];
-  int koff[DK], voff[D / 32];
+  int koff[DK], voff[NDT];
   uint4 vreg[VPER];
 
   __device__ __forceinline__ void setup() {
@@ -150,12 +152,12 @@ struct Attn {
       koff[ks] = r16 * RB + k_unit<DT, D, BLK>(r16, (DT == kFP8 ? 0 : ks * 4) + g) * LB;
     // V^T (A operand) via ds_read_b64_tr_b16: in lane group g, lane r16 supplies
     // row 4g + r16 / 4 (a key) and columns 4 (r16 % 4) .. + 3 of a 16-wide d
-    // tile; odd d tiles sit 32 bytes after even ones (same 64-byte group).
+    // tile dt.
     const int vr = 4 * g + (r16 >> 2), vq = r16 & 3;
 #pragma unroll
-    for (int dp = 0; dp < D / 32; ++dp) {
-      const int dcol = dp * 32 + vq * 4;
-      voff[dp] = vr * (D * 2) + v_chunk<D>(vr, dcol >> 3) * 16 + (dcol & 7) * 2;
+    for (int dt = 0; dt < NDT; ++dt) {
+      const int dcol = dt * 16 + vq * 4;
+      voff[dt] = vr * (D * 2) + v_chunk<D>(vr, dcol >> 3) * 16 + (dcol & 7) * 2;
     }
   }
 
@@ -252,7 +254,7 @@ struct Attn {
   // V^T fragment of d tile dt for PV step j: keys j*32 + 4g + [0,4) and
   // j*32 + 16 + 4g + [0,4), matching the P^T slots of the lane.
   __device__ __forceinline__ bf16x8 load_v(const uint16_t *__restrict__ Vb, int j, int dt) {
-    const uint8_t *p0 = (const uint8_t *)Vb + voff[dt / 2] + (dt % 2) * 32 + j * 32 * (D * 2);
+    const uint8_t *p0 = (const uint8_t *)Vb + voff[dt] + j * 32 * (D * 2);
     const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4 *)p0);
     const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4 *)(p0 + 16 * D * 2));
     return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
