@@ -74,6 +74,19 @@ def test_sparse_ragged_shapes(dtype, d, block, seq):
     full_check(c)
 
 
+@pytest.mark.parametrize("dtype,hq,hkv,seq", [
+    ("bf16", 6, 3, 900), ("fp8", 6, 3, 900), ("bf16", 7, 7, 640), ("bf16", 12, 6, 1280),
+    ("fp8", 10, 5, 1024), ("bf16", 16, 16, 512),
+])
+def test_head_layouts_outside_the_xcd_grouping(dtype, hq, hkv, seq):
+    """Head counts whose kv groups do not divide the 8 XCDs (the plain
+    workgroup order) and large MHA: every row against the oracle."""
+    announce(f"heads {hq}/{hkv} {dtype} seq={seq}")
+    c = gen.make_case(hq, hkv, seq, 128, 128, dtype, 300 + hq + seq, gamma=0.2, rope=True,
+                      n_vert=4, slash=True, block_offset=1.0)
+    full_check(c)
+
+
 @pytest.mark.parametrize("dtype", ["bf16", "fp8"])
 def test_config_shape_4k_sampled(dtype):
     """Config 1 (or config 4's heads/dtype) at seq 4096: every head, sampled rows."""
