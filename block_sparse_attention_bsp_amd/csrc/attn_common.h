@@ -24,15 +24,6 @@ __device__ __forceinline__ void lds_dma16(__amdgpu_buffer_rsrc_t rs, uint32_t vo
                                            voff, soff, 0, 0);
 }
 
-// Packed variable-length batch over a paged K/V cache: sequence s owns
-// tokens cu_seqlens[s] .. cu_seqlens[s+1] of q / o / lse and query blocks
-// cu_blocks[s] .. cu_blocks[s+1] of the grid; key block J of sequence s is
-// cache page page_table[s * max_pages + J], laid out [page][hkv][BLK][d].
-struct VarlenDev {
-  const int32_t *cu_seqlens, *cu_blocks, *page_table, *block_order;
-  int nseq, max_pages, idx_stride;
-};
-
 // Workgroup bid -> (query block I, q head h), heaviest rows first.
 //   xcd_map == 0: plain order.
 //   xcd_map >= hkv: XCD x = bid % 8 (the hardware's round-robin) serves kv
@@ -86,7 +77,7 @@ struct AttnRow {
 };
 
 template <bool VL>
-__device__ __forceinline__ AttnRow attn_locate(int I, int seq, int nb, const VarlenDev &vl) {
+__device__ __forceinline__ AttnRow attn_locate(int I, int seq, int nb, const VarlenArgs &vl) {
   AttnRow r{I, I, 0, seq, nb, nullptr};
   if constexpr (VL) {
     // launch order: the caller's permutation (heaviest first), if given

@@ -378,7 +378,7 @@ __global__ __launch_bounds__(BLK * 2, (BLK == 64 && D == 128) ? 1 : 2) void attn
     const int32_t *__restrict__ kv_idx, const int32_t *__restrict__ kv_cnt,
     uint16_t *__restrict__ o, float *__restrict__ lse, const float *__restrict__ q_scale,
     const float *__restrict__ k_scale, const float *__restrict__ v_scale, int hq, int hkv,
-    int seq, int nb, float sm_scale_log2, int xcd_map, VarlenDev vl) {
+    int seq, int nb, float sm_scale_log2, int xcd_map, VarlenArgs vl) {
   using A = Attn<DT, D, BLK>;
   using C = typename A::C;
   constexpr int RB = C::RB, LB = C::LB, DK = C::DK, KT = C::KT, NSUB = C::NSUB;
@@ -528,7 +528,7 @@ static hipError_t launch_t(const Shape &s, const AttnArgs &a, hipStream_t st) {
   hipLaunchKernelGGL((attn_mfma_kernel<DT, D, BLK, false>), dim3((unsigned)items), dim3(BLK * 2),
                      0, st, (const uint8_t *)a.q, (const uint8_t *)a.k, (const uint8_t *)a.v,
                      a.kv_idx, a.kv_cnt, (uint16_t *)a.o, a.lse, a.q_scale, a.k_scale, a.v_scale,
-                     s.hq, s.hkv, s.seq, s.nb, a.sm_scale * kLog2e, xcd, VarlenDev{});
+                     s.hq, s.hkv, s.seq, s.nb, a.sm_scale * kLog2e, xcd, VarlenArgs{});
   return hipGetLastError();
 }
 
@@ -539,12 +539,10 @@ static hipError_t launch_vl_t(const Shape &s, const AttnArgs &a, const VarlenArg
   const long items = (long)s.hq * s.nb;
   // a row reads only its own sequence's pages: all groups at once
   const int xcd = attn_xcd_mode(s, 0);
-  const VarlenDev vd{v.cu_seqlens, v.cu_blocks, v.page_table, v.block_order,
-                     v.nseq,       v.max_pages, v.idx_stride};
   hipLaunchKernelGGL((attn_mfma_kernel<DT, D, BLK, true>), dim3((unsigned)items), dim3(BLK * 2),
                      0, st, (const uint8_t *)a.q, (const uint8_t *)a.k, (const uint8_t *)a.v,
                      a.kv_idx, a.kv_cnt, (uint16_t *)a.o, a.lse, a.q_scale, a.k_scale, a.v_scale,
-                     s.hq, s.hkv, s.seq, s.nb, a.sm_scale * kLog2e, xcd, vd);
+                     s.hq, s.hkv, s.seq, s.nb, a.sm_scale * kLog2e, xcd, v);
   return hipGetLastError();
 }
 

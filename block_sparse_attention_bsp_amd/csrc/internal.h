@@ -34,6 +34,12 @@ hipError_t launch_mask(const Shape &s, float gamma, int sink_blocks, int local_b
                        const float *score, const uint8_t *user_mask, uint8_t *mask,
                        int32_t *kv_idx, int32_t *kv_cnt, hipStream_t st,
                        const float *rescue = nullptr, float gamma_r = 0.f);
+// Packed variable-length batch over a paged K/V cache (passed to kernels by
+// value): sequence s owns tokens cu_seqlens[s] .. cu_seqlens[s+1] of q / o /
+// lse and query blocks cu_blocks[s] .. cu_blocks[s+1] of the batch; key
+// block J of sequence s is cache page page_table[s * max_pages + J], laid out
+// [page][hkv][block][d]; kv lists and score / mask rows have stride
+// idx_stride; block_order is an optional launch order of the batch's blocks.
 struct VarlenArgs {
   const int32_t *cu_seqlens, *cu_blocks, *page_table, *block_order;
   int nseq, max_pages, idx_stride;
