@@ -1,28 +1,12 @@
-// Pieces shared by the MFMA attention kernels (bf16 and fp8): buffer
-// descriptors and direct-to-LDS loads, the order in which workgroups take
-// (q head, query block) rows, the packed-batch lookup, and the stream of a
-// row's kept key-block list.
+// Pieces shared by the MFMA attention kernels (bf16 and fp8): the order in
+// which workgroups take (q head, query block) rows, the packed-batch lookup,
+// and the stream of a row's kept key-block list.
 #pragma once
 
 #include "device.h"
 #include "internal.h"
 
 namespace bsp {
-
-// Buffer descriptor over [base, base + bytes): raw (stride 0), untyped
-// 32-bit data format as gfx9-family untyped buffer loads expect.
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, uint32_t bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes,
-                                           0x00020000);
-}
-
-// 16 bytes per lane from rsrc + soff + voff straight into LDS at ldst + 16 * lane
-// (buffer_load_dwordx4 ... lds): no VGPR staging and no 64-bit address math.
-__device__ __forceinline__ void lds_dma16(__amdgpu_buffer_rsrc_t rs, uint32_t voff, uint32_t soff,
-                                          void *ldst) {
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (__attribute__((address_space(3))) void *)ldst, 16,
-                                           voff, soff, 0, 0);
-}
 
 // Workgroup bid -> (query block I, q head h), heaviest rows first.
 //   xcd_map == 0: plain order.

@@ -61,6 +61,21 @@ __device__ __forceinline__ uint32_t f32_to_bf16_bits(float x) {
   return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
 }
 
+// Buffer descriptor over [base, base + bytes): raw (stride 0), untyped
+// 32-bit data format as gfx9-family untyped buffer loads expect.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes,
+                                           0x00020000);
+}
+
+// 16 bytes per lane from rsrc + soff + voff straight into LDS at ldst + 16 * lane
+// (buffer_load_dwordx4 ... lds): no VGPR staging and no 64-bit address math.
+__device__ __forceinline__ void lds_dma16(__amdgpu_buffer_rsrc_t rs, uint32_t voff, uint32_t soff,
+                                          void *ldst) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (__attribute__((address_space(3))) void *)ldst, 16,
+                                           voff, soff, 0, 0);
+}
+
 // Packed variable-length batch: the sequence whose query blocks
 // cu_blocks[s] .. cu_blocks[s+1] contain batch block gb (binary search over
 // the nseq + 1 nondecreasing offsets).

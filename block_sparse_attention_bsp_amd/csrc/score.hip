@@ -5,10 +5,10 @@
 // global normalisation).
 //
 // Two passes over the causal block grid of a group of 32 query blocks:
-//   pass 1  S^T tiles = Kbar Qbar^T (32 key blocks x 32 query blocks) on
-//           v_mfma_f32_32x32x2_f32 - fp32 products and sums, so the
-//           threshold downstream sees full-precision scores - reduced to the
-//           running row max and sum of exp;
+//   pass 1  S^T tiles = Kbar Qbar^T (32 key blocks x 32 query blocks), with
+//           fp32-accurate products and sums so that the threshold downstream
+//           sees full-precision scores, reduced to the running row max and
+//           sum of exp;
 //   pass 2  after the row statistics meet, P = exp(S - max) / sum on the
 //           causal part, zeros above it.
 // Each lane owns one query block (a column of S^T), so the row reductions are
@@ -24,9 +24,11 @@
 // score_kernel_reg (rows of at most 1024 blocks): eight wavefronts with at
 // most four tiles each keep their raw scores in registers, so P is written
 // once, normalised, through an LDS transpose that makes every store cover
-// whole 128-byte row runs.  score_kernel (longer rows): four wavefronts write
-// the raw scores transposed the same way, then the workgroup sweeps its rows
-// row-major with 16-byte accesses and normalises them in place.
+// whole 128-byte row runs; its products run on bf16 matrix cores over three
+// bf16 planes of each operand.  score_kernel (longer rows): four wavefronts on
+// v_mfma_f32_32x32x2_f32 write the raw scores transposed the same way, then
+// the workgroup sweeps its rows row-major with 16-byte accesses and
+// normalises them in place.
 #include "device.h"
 #include "internal.h"
 
@@ -237,116 +239,217 @@ __global__ __launch_bounds__(256) void score_kernel(const float *__restrict__ q_
   }
 }
 
+// fp32 -> three bf16 planes, x = hi + mid + lo exactly: each plane is the
+// bf16 rounding (to nearest even) of what the planes before it leave, every
+// such remainder is exact in fp32, and the last one has at most 8
+// significant bits.  A product of two planes is exact in fp32.  Pairs of
+// elements share one conversion (v_cvt_pk_bf16_f32) and fill one register of
+// each plane; a remainder x - plane is one v_dot2c_f32_bf16 of the packed
+// plane with (-1, 0) or (0, -1) accumulated onto x (exact, as the difference
+// is representable).  The two constants are kept opaque in registers: folded,
+// (-1, 0) becomes the inline constant -1.0, which the hardware does not read
+// as that bf16 pair (the scores came out wrong).
+__device__ __forceinline__ void split3(const float (&x)[8], bf16x8 &hi, bf16x8 &mi, bf16x8 &lo) {
+  uint32_t b0 = 0x0000bf80u, b1 = 0xbf800000u;  // bf16 pairs (-1, 0) and (0, -1)
+  asm volatile("" : "+v"(b0), "+v"(b1));
+  bf16x2 n0, n1;
+  __builtin_memcpy(&n0, &b0, 4);
+  __builtin_memcpy(&n1, &b1, 4);
+#pragma unroll
+  for (int e = 0; e < 8; e += 2) {
+    const bf16x2 h = __builtin_convertvector((f32x2{x[e], x[e + 1]}), bf16x2);
+    const float r0 = __builtin_amdgcn_fdot2_f32_bf16(h, n0, x[e], false);
+    const float r1 = __builtin_amdgcn_fdot2_f32_bf16(h, n1, x[e + 1], false);
+    const bf16x2 m = __builtin_convertvector((f32x2{r0, r1}), bf16x2);
+    const float s0 = __builtin_amdgcn_fdot2_f32_bf16(m, n0, r0, false);
+    const float s1 = __builtin_amdgcn_fdot2_f32_bf16(m, n1, r1, false);
+    const bf16x2 l = __builtin_convertvector((f32x2{s0, s1}), bf16x2);
+    hi[e] = h[0], hi[e + 1] = h[1];
+    mi[e] = m[0], mi[e + 1] = m[1];
+    lo[e] = l[0], lo[e + 1] = l[1];
+  }
+}
+
 // Rows of at most 1024 key blocks: eight wavefronts split the key-block tiles
 // of the group (at most four each) and keep their raw scores in registers,
 // so P is written once, already normalised, and never read back.
+//
+// The dot products run on v_mfma_f32_32x32x16_bf16 over three bf16 planes of
+// each operand: hi*hi + hi*mid + mid*hi + hi*lo + lo*hi + mid*mid leaves out
+// only terms below 2^-24 of each product, every plane product is exact and
+// the sums are fp32, so the scores are as accurate as fp32 products (the
+// threshold downstream needs them to well under its 1e-4 band), at 1/2.7 of
+// the matrix-core time of v_mfma_f32_32x32x2_f32.  The Qbar planes are made
+// once and stay in registers; each Kbar tile is split as it is read.
+//
+// Kbar tiles reach LDS by direct-to-LDS buffer loads in two halves of the
+// dimensions (each a wavefront's private buffer), the next half issued
+// before the current one is computed.  Lane (r, kg) = (lane % 32, lane / 32)
+// reads row r, dimensions D/2*kg + 8s .. + 8 at MFMA step s; a half holds
+// steps [D/32 * hh, D/32 * (hh + 1)) as D/8 chunks of 16 bytes per row, in
+// rows padded by one chunk: the odd row stride in 16-byte units puts the 16
+// lanes of a ds_read_b128 phase on 16 distinct bank groups, and every read
+// is the lane's row base plus an immediate offset.
+template <int D>
+struct ScoreStage {
+  static constexpr int CPR = D / 8;                  // chunks per row of a half
+  static constexpr int RS = (CPR + 1) * 16;          // padded row stride (bytes)
+  static constexpr int NDMA = (32 * (CPR + 1) + 63) / 64;  // loads per half and wavefront
+  static constexpr int HB = NDMA * 1024;             // bytes per half buffer
+};
+
+// The MFMA steps of one staged half hh: lane (l32, half) reads row l32 of
+// the half buffer, splits it and accumulates the six plane products (the
+// small ones into their own accumulator, unless ONE: the rescue variant needs
+// those registers).  buf is restrict-qualified so that the compiler knows the
+// loads in flight into the other half do not alias it.
+template <int D, bool ONE>
+__device__ __forceinline__ void score_half(const uint8_t *__restrict__ buf, int hh, int half,
+                                           int l32, const bf16x8 (&qh)[D / 16],
+                                           const bf16x8 (&qm)[D / 16], const bf16x8 (&ql)[D / 16],
+                                           f32x16 &big, f32x16 &small) {
+  constexpr int SU = D / 32;
+  using S = ScoreStage<D>;
+  const uint8_t *arow = buf + l32 * S::RS + half * (S::CPR / 2) * 16;
+#pragma unroll
+  for (int sl = 0; sl < SU; ++sl) {
+    const int s = hh * SU + sl;
+    const float4 a0 = *(const float4 *)(arow + 32 * sl);
+    const float4 a1 = *(const float4 *)(arow + 32 * sl + 16);
+    const float x[8] = {a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w};
+    bf16x8 ah, am, al;
+    split3(x, ah, am, al);
+    f32x16 &sm = ONE ? big : small;
+    sm = __builtin_amdgcn_mfma_f32_32x32x16_bf16(am, qm[s], sm, 0, 0, 0);
+    sm = __builtin_amdgcn_mfma_f32_32x32x16_bf16(al, qh[s], sm, 0, 0, 0);
+    sm = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ah, ql[s], sm, 0, 0, 0);
+    sm = __builtin_amdgcn_mfma_f32_32x32x16_bf16(am, qh[s], sm, 0, 0, 0);
+    sm = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ah, qm[s], sm, 0, 0, 0);
+    big = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ah, qh[s], big, 0, 0, 0);
+  }
+}
+
 template <int D, bool RESC>
 __global__ __launch_bounds__(512) void score_kernel_reg(const float *__restrict__ q_pool,
                                                         const float *__restrict__ k_pool,
                                                         const float *__restrict__ k_radius,
                                                         float *__restrict__ P, int hq, int hkv,
                                                         int nb, float c2) {
-  constexpr int KS = D / 2;   // k-steps; step ks, lane half h <-> dimension ks + KS*h
+  using S = ScoreStage<D>;
   constexpr int NWV = 8;      // wavefronts
   constexpr int MAXT = 4;     // tiles per wavefront
+  constexpr int NS = D / 16;  // MFMA steps per tile (16 dimensions each)
+  constexpr int CPR = S::CPR, NDMA = S::NDMA;
+  static_assert(S::HB >= 32 * 33 * 4, "the pass-2 transpose reuses a half buffer");
   __shared__ float red_m[NWV][32], red_l[NWV][32], row_m[32], row_inv[32];
-  __shared__ __attribute__((aligned(16))) float kt_s[NWV * 32 * (D + 4)];
+  // one array per half, so the compiler sees that a load into one half
+  // cannot alias reads of the other and does not wait for it
+  __shared__ __attribute__((aligned(16))) uint8_t stg0[NWV][S::HB];
+  __shared__ __attribute__((aligned(16))) uint8_t stg1[NWV][S::HB];
   const int G = (nb + 31) / 32;
   const int grp = G - 1 - (int)blockIdx.y;
   const int h = blockIdx.x;
   const int g = h / (hq / hkv);
-  const int w = threadIdx.x >> 6, lane = threadIdx.x & 63, half = lane >> 5, l32 = lane & 31;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63, half = lane >> 5, l32 = lane & 31;
   const int I0 = grp * 32;
   const int rows = min(32, nb - I0);
   const int Il = I0 + l32;  // this lane's query block
   const bool row_ok = l32 < rows;
   const int ntc = (I0 + rows - 1) / 32 + 1;  // key-block tiles touching the causal part
+  const int nt = w < ntc ? min(MAXT, (ntc - w + NWV - 1) / NWV) : 0;  // this wave's tiles
   const bool vec = (nb & 3) == 0;             // rows of P are 16-byte aligned
   float *pgrp = P + ((size_t)h * nb + I0) * nb;
 
-  float qb[KS];
-  {
-    const float *src = q_pool + ((size_t)h * nb + min(Il, nb - 1)) * D + KS * half;
+  // direct-to-LDS staging: load it of a half puts the lane's 16 bytes at
+  // position it * 64 + lane = row * (CPR + 1) + chunk of the wavefront's
+  // buffer; the padding chunk and the positions past row 31 take a copy of
+  // an in-bounds chunk that is never read
+  const __amdgpu_buffer_rsrc_t krs =
+      make_rsrc(k_pool + (size_t)g * nb * D, (uint32_t)((size_t)nb * D * 4));
+  int vrow[NDMA];        // source row of each load
+  uint32_t vdim[NDMA];   // its byte offset inside the row
 #pragma unroll
-    for (int i = 0; i < KS; i += 4) {
-      const float4 t = *(const float4 *)(src + i);
-      qb[i] = row_ok ? t.x : 0.f;
-      qb[i + 1] = row_ok ? t.y : 0.f;
-      qb[i + 2] = row_ok ? t.z : 0.f;
-      qb[i + 3] = row_ok ? t.w : 0.f;
-    }
+  for (int it = 0; it < NDMA; ++it) {
+    const int p = it * 64 + lane, c = p % (CPR + 1);
+    const int cc = c < CPR ? c : 0;
+    const int kg = cc / (CPR / 2), rem = cc % (CPR / 2);
+    vrow[it] = min(p / (CPR + 1), 31);
+    vdim[it] = (uint32_t)((D / 2) * kg + 4 * rem) * 4;
   }
-  // rescue branch: |Qbar_I| (the lane holds half of the dimensions)
-  float qn = 0.f;
-  if constexpr (RESC) {
+  // unit u = half u % 2 of the wavefront's tile u / 2 (key blocks jt*32 ..)
+  // into buffer u % 2.  Rows past the last key block re-read it (a clamp,
+  // not a branch: the compiler's wait tracking then sees every load in
+  // flight and lets the reads of the other buffer go ahead).
+  auto issue = [&](int u) {
+    const int jt = w + NWV * (u >> 1);
+    const uint32_t soff = (uint32_t)(jt * 32 * D + (u & 1) * (D / 4)) * 4;
+    uint8_t *dst = (u & 1) ? &stg1[w][0] : &stg0[w][0];
+    const int last = nb - 1 - jt * 32;
+#pragma unroll
+    for (int it = 0; it < NDMA; ++it)
+      lds_dma16(krs, (uint32_t)min(vrow[it], last) * (D * 4) + vdim[it], soff, dst + it * 1024);
+  };
+  // the first Kbar half goes out before the Qbar loads, so the two latencies overlap
+  if (nt > 0) issue(0);
+
+  // B operand (Qbar^T) planes: lane (n, kg) holds Qbar[I0 + n] at dimensions
+  // D/2*kg + 8s .. + 8 for step s
+  bf16x8 qh[NS], qm[NS], ql[NS];
+  float qn = 0.f;  // rescue branch: |Qbar_I|
+  {
+    const float *src = q_pool + ((size_t)h * nb + min(Il, nb - 1)) * D + (D / 2) * half;
     float ss = 0.f;
 #pragma unroll
-    for (int i = 0; i < KS; ++i) ss = fmaf(qb[i], qb[i], ss);
-    qn = sqrtf(ss + __shfl_xor(ss, 32, 64));
+    for (int s = 0; s < NS; ++s) {
+      const float4 t0 = *(const float4 *)(src + 8 * s), t1 = *(const float4 *)(src + 8 * s + 4);
+      float x[8] = {t0.x, t0.y, t0.z, t0.w, t1.x, t1.y, t1.z, t1.w};
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        x[e] = row_ok ? x[e] : 0.f;
+        if constexpr (RESC) ss = fmaf(x[e], x[e], ss);
+      }
+      split3(x, qh[s], qm[s], ql[s]);
+    }
+    if constexpr (RESC) qn = sqrtf(ss + __shfl_xor(ss, 32, 64));
   }
   const float *rad = RESC ? k_radius + (size_t)g * nb : nullptr;
-
-  constexpr int TF4 = 32 * D / 4 / 64;  // float4 per lane per tile
-  constexpr int RS = D + 4;             // padded LDS row stride (floats)
-  constexpr int TS = 33;                // transpose row stride (floats)
-  float *kt_lds = kt_s + w * 32 * RS;
-  // the tile goes global -> registers -> LDS in two halves (no prefetch:
-  // the SIMD's other wavefront covers the load latency)
-  auto load_stage = [&](int jt) {
-    const float *src = k_pool + ((size_t)g * nb + jt * 32) * D;
-    const int n = min(32, nb - jt * 32);
-#pragma unroll
-    for (int hb = 0; hb < 2; ++hb) {
-      float4 st[TF4 / 2];
-#pragma unroll
-      for (int i = 0; i < TF4 / 2; ++i) {
-        const int f = lane + 64 * (hb * (TF4 / 2) + i);
-        st[i] = f / (D / 4) < n ? *(const float4 *)(src + 4 * f) : make_float4(0.f, 0.f, 0.f, 0.f);
-      }
-#pragma unroll
-      for (int i = 0; i < TF4 / 2; ++i) {
-        const int f = lane + 64 * (hb * (TF4 / 2) + i);
-        *(float4 *)(kt_lds + (f / (D / 4)) * RS + (f % (D / 4)) * 4) = st[i];
-      }
-    }
-  };
-  auto mma = [&]() -> f32x16 {
-    const float *arow = kt_lds + l32 * RS + KS * half;
-    f32x16 acc = f32x16{};
-#pragma unroll
-    for (int i = 0; i < KS / 4; ++i) {
-      const float4 a = *(const float4 *)(arow + 4 * i);
-      acc = __builtin_amdgcn_mfma_f32_32x32x2f32(a.x, qb[4 * i], acc, 0, 0, 0);
-      acc = __builtin_amdgcn_mfma_f32_32x32x2f32(a.y, qb[4 * i + 1], acc, 0, 0, 0);
-      acc = __builtin_amdgcn_mfma_f32_32x32x2f32(a.z, qb[4 * i + 2], acc, 0, 0, 0);
-      acc = __builtin_amdgcn_mfma_f32_32x32x2f32(a.w, qb[4 * i + 3], acc, 0, 0, 0);
-    }
-    return acc;
-  };
 
   // ---- pass 1: raw log2-domain scores held in registers, row max and sum
   float held[MAXT][16];
   float m = -INFINITY, l = 0.f;
 #pragma unroll
   for (int t = 0; t < MAXT; ++t) {
-    const int jt = w + t * NWV;
-    if (jt < ntc) {
-      load_stage(jt);
-      const f32x16 acc = mma();
+    if (t < nt) {
+      const int jt = w + NWV * t;
+      f32x16 big = f32x16{}, small = f32x16{};
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh) {
+        const int u = 2 * t + hh;
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        // after the last unit the idle buffer takes a repeat of unit u - 1
+        // (never read): every unit issues exactly one load group
+        issue(u + 1 < 2 * nt ? u + 1 : u - 1);
+        __builtin_amdgcn_sched_barrier(0);  // the loads go out before the MFMAs
+        score_half<D, RESC>(hh ? &stg1[w][0] : &stg0[w][0], hh, half, l32, qh, qm, ql, big, small);
+      }
+      // only the diagonal tile (and a ragged last one) has entries to mask
+      const bool edge = jt * 32 + 31 > I0 || jt * 32 + 31 >= nb;
       float tmax = -INFINITY;
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int J = jt * 32 + (r / 4) * 8 + half * 4 + (r % 4);
         const float add = RESC && J < nb ? qn * rad[J] : 0.f;
-        held[t][r] = (J <= Il && J < nb) ? (acc[r] + add) * c2 : -INFINITY;
+        const float x = (big[r] + small[r] + add) * c2;
+        held[t][r] = (!edge || (J <= Il && J < nb)) ? x : -INFINITY;
         tmax = fmaxf(tmax, held[t][r]);
       }
       const float mn = fmaxf(m, tmax);
       if (mn != -INFINITY) {
         float acc_l = 0.f;
 #pragma unroll
-        for (int r = 0; r < 16; ++r) acc_l += exp2f(held[t][r] - mn);
-        l = l * exp2f(m - mn) + acc_l;
+        for (int r = 0; r < 16; ++r) acc_l += __builtin_amdgcn_exp2f(held[t][r] - mn);
+        l = l * __builtin_amdgcn_exp2f(m - mn) + acc_l;
         m = mn;
       }
     }
@@ -355,7 +458,8 @@ __global__ __launch_bounds__(512) void score_kernel_reg(const float *__restrict_
     const float mo = __shfl_xor(m, 32, 64), lo = __shfl_xor(l, 32, 64);
     const float mn = fmaxf(m, mo);
     if (mn != -INFINITY) {
-      l = (m == -INFINITY ? 0.f : l * exp2f(m - mn)) + (mo == -INFINITY ? 0.f : lo * exp2f(mo - mn));
+      l = (m == -INFINITY ? 0.f : l * __builtin_amdgcn_exp2f(m - mn)) +
+          (mo == -INFINITY ? 0.f : lo * __builtin_amdgcn_exp2f(mo - mn));
       m = mn;
     }
   }
@@ -371,7 +475,8 @@ __global__ __launch_bounds__(512) void score_kernel_reg(const float *__restrict_
     float L = 0.f;
 #pragma unroll
     for (int i = 0; i < NWV; ++i)
-      if (red_m[i][l32] != -INFINITY) L += red_l[i][l32] * exp2f(red_m[i][l32] - M);
+      if (red_m[i][l32] != -INFINITY)
+        L += red_l[i][l32] * __builtin_amdgcn_exp2f(red_m[i][l32] - M);
     row_m[l32] = M;
     row_inv[l32] = L > 0.f ? 1.f / L : 0.f;
   }
@@ -380,15 +485,18 @@ __global__ __launch_bounds__(512) void score_kernel_reg(const float *__restrict_
   // ---- pass 2: normalise the held tiles and write them through the wave's
   // LDS slice, so that 8 lanes cover one row's 32 keys of a tile
   {
+    constexpr int TS = 33;  // transpose row stride (floats)
+    float *kt_lds = (float *)&stg0[w][0];
     const float M = row_m[l32], inv = row_inv[l32];
     const int c4 = (lane & 7) * 4;
 #pragma unroll
     for (int t = 0; t < MAXT; ++t) {
       const int jt = w + t * NWV;
-      if (jt < ntc) {
+      if (t < nt) {
 #pragma unroll
         for (int r = 0; r < 16; ++r)
-          kt_lds[l32 * TS + (r / 4) * 8 + half * 4 + (r % 4)] = exp2f(held[t][r] - M) * inv;
+          kt_lds[l32 * TS + (r / 4) * 8 + half * 4 + (r % 4)] =
+              __builtin_amdgcn_exp2f(held[t][r] - M) * inv;
 #pragma unroll
         for (int it = 0; it < 4; ++it) {
           const int rr = it * 8 + (lane >> 3);

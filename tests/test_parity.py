@@ -219,6 +219,53 @@ def test_rescue_branch_matches_oracle(which):
     print(f"  kept {om.sum()} (base alone {base}), band blocks {nband}", flush=True)
 
 
+def _pooled_accuracy_case(which):
+    """Planted block offsets (scores spread over several logits), several
+    32-block tiles with a ragged last one."""
+    dtype, d, block, nb = which.split("_")
+    d, block, nb = int(d), int(block), int(nb)
+    return gen.make_case(4, 2, block * nb - block // 3, d, block, dtype, 11 + nb, gamma=0.2,
+                         n_vert=4, block_offset=1.5)
+
+
+@pytest.mark.parametrize("which", ["f32_64_64_100", "bf16_128_128_70", "fp8_128_128_45",
+                                   "bf16_64_128_130"])
+@pytest.mark.parametrize("rescue", [False, True])
+def test_pooled_scores_at_fp32_accuracy(which, rescue):
+    """The pooled scores are as accurate as fp32 dot products.
+
+    Where P is at least 1e-6 of its row maximum, log P is within
+    2e-6 + 2^-20 * c * sum_i |Qbar_i Kbar_i| of the fp64 oracle: the size of
+    an fp32 accumulation error.  Products that drop a bf16 plane term err by
+    about 2^-16 of that sum, sixteen times the bound."""
+    announce(f"pooled score accuracy {which} rescue={rescue}")
+    c = _pooled_accuracy_case(which)
+    d = H.dev(c)
+    qp, kp, sc = bsp.score(d["q"], d["k"], c.block, q_scale=d["q_scale"], k_scale=d["k_scale"])
+    cs = 1.0 / math.sqrt(c.d)
+    qb = oracle.pool(c.q, c.dtype, c.block, c.q_scale)
+    kb = oracle.pool(c.k, c.dtype, c.block, c.k_scale)
+    grp = c.hq // c.hkv
+    mag = np.stack([np.abs(qb[h]) @ np.abs(kb[h // grp]).T for h in range(c.hq)]) * cs
+    if rescue:
+        kr, sc = bsp.score_rescue(d["k"], qp, kp, c.seq, c.block, k_scale=d["k_scale"])
+        r = oracle.key_radius(c.k, c.dtype, c.block, c.k_scale)
+        _, P = oracle.score_rescue(qb, kb, r, cs)
+        qn = np.sqrt((qb.astype(np.float64) ** 2).sum(-1))
+        mag = mag + cs * qn[:, :, None] * r[np.arange(c.hq) // grp][:, None, :]
+    else:
+        _, P = oracle.score(qb, kb, cs)
+    torch.cuda.synchronize()
+    G = sc.cpu().numpy().astype(np.float64)
+    sel = P >= 1e-6 * P.max(-1, keepdims=True)
+    sel &= np.tril(np.ones(P.shape[-2:], bool))[None]
+    err = np.abs(np.log(G[sel]) - np.log(P[sel]))
+    tol = 2e-6 + 2.0 ** -20 * mag[sel]
+    worst = float((err / tol).max())
+    print(f"  nb {c.nb} max |dlog P| {err.max():.2e}, worst err/tol {worst:.3f}", flush=True)
+    assert worst <= 1.0
+
+
 def test_long_rows_over_2048_blocks():
     """nb = 2188: the general score kernel and the general mask path, base and
     rescue branches, against the oracle."""
