@@ -239,37 +239,6 @@ __global__ __launch_bounds__(256) void score_kernel(const float *__restrict__ q_
   }
 }
 
-// fp32 -> three bf16 planes, x = hi + mid + lo exactly: each plane is the
-// bf16 rounding (to nearest even) of what the planes before it leave, every
-// such remainder is exact in fp32, and the last one has at most 8
-// significant bits.  A product of two planes is exact in fp32.  Pairs of
-// elements share one conversion (v_cvt_pk_bf16_f32) and fill one register of
-// each plane; a remainder x - plane is one v_dot2c_f32_bf16 of the packed
-// plane with (-1, 0) or (0, -1) accumulated onto x (exact, as the difference
-// is representable).  The two constants are kept opaque in registers: folded,
-// (-1, 0) becomes the inline constant -1.0, which the hardware does not read
-// as that bf16 pair (the scores came out wrong).
-__device__ __forceinline__ void split3(const float (&x)[8], bf16x8 &hi, bf16x8 &mi, bf16x8 &lo) {
-  uint32_t b0 = 0x0000bf80u, b1 = 0xbf800000u;  // bf16 pairs (-1, 0) and (0, -1)
-  asm volatile("" : "+v"(b0), "+v"(b1));
-  bf16x2 n0, n1;
-  __builtin_memcpy(&n0, &b0, 4);
-  __builtin_memcpy(&n1, &b1, 4);
-#pragma unroll
-  for (int e = 0; e < 8; e += 2) {
-    const bf16x2 h = __builtin_convertvector((f32x2{x[e], x[e + 1]}), bf16x2);
-    const float r0 = __builtin_amdgcn_fdot2_f32_bf16(h, n0, x[e], false);
-    const float r1 = __builtin_amdgcn_fdot2_f32_bf16(h, n1, x[e + 1], false);
-    const bf16x2 m = __builtin_convertvector((f32x2{r0, r1}), bf16x2);
-    const float s0 = __builtin_amdgcn_fdot2_f32_bf16(m, n0, r0, false);
-    const float s1 = __builtin_amdgcn_fdot2_f32_bf16(m, n1, r1, false);
-    const bf16x2 l = __builtin_convertvector((f32x2{s0, s1}), bf16x2);
-    hi[e] = h[0], hi[e + 1] = h[1];
-    mi[e] = m[0], mi[e + 1] = m[1];
-    lo[e] = l[0], lo[e + 1] = l[1];
-  }
-}
-
 // Rows of at most 1024 key blocks: eight wavefronts split the key-block tiles
 // of the group (at most four each) and keep their raw scores in registers,
 // so P is written once, already normalised, and never read back.

@@ -121,16 +121,10 @@ __global__ __launch_bounds__(BLK * 2) void score_arith_kernel(
         *(float4 *)((float *)kt + r * RSF + c4) = x;
       } else {
         // hi + mid + lo, each the bf16 rounding (to nearest even) of what the
-        // planes before it leave; every difference is exact in fp32
+        // planes before it leave; every difference is exact in fp32 (split3)
         const float xs[4] = {x.x, x.y, x.z, x.w};
         bf16x4 hv, mv, lv;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          hv[e] = (__bf16)xs[e];
-          const float r1 = xs[e] - (float)hv[e];
-          mv[e] = (__bf16)r1;
-          lv[e] = (__bf16)(r1 - (float)mv[e]);
-        }
+        split3(xs, hv, mv, lv);
         uint8_t *base = kt + r * RSB + c4 * 2;
         __builtin_memcpy(base, &hv, 8);
         __builtin_memcpy(base + C::PLANE, &mv, 8);
