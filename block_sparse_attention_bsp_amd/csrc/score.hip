@@ -21,223 +21,17 @@
 // abstract) the same kernels compute c (Qbar_I . Kbar_J + |Qbar_I| r_J), an
 // upper bound on the block's best per-key logit, and its row softmax.
 //
-// score_kernel_reg (rows of at most 1024 blocks): eight wavefronts with at
-// most four tiles each keep their raw scores in registers, so P is written
-// once, normalised, through an LDS transpose that makes every store cover
-// whole 128-byte row runs; its products run on bf16 matrix cores over three
-// bf16 planes of each operand.  score_kernel (longer rows): four wavefronts on
-// v_mfma_f32_32x32x2_f32 write the raw scores transposed the same way, then
-// the workgroup sweeps its rows row-major with 16-byte accesses and
-// normalises them in place.
+// Both kernels form the products on bf16 matrix cores over three bf16 planes
+// of each operand.  score_kernel_reg (rows of at most 1024 blocks): eight
+// wavefronts with at most four tiles each keep their raw scores in
+// registers, so P is written once, normalised, through an LDS transpose that
+// makes every store cover whole 128-byte row runs.  score_kernel_2p (longer
+// rows): pass 2 recomputes the tiles instead of holding them, and writes P
+// once from the MFMA layout.
 #include "device.h"
 #include "internal.h"
 
 namespace bsp {
-
-template <int D, bool RESC>
-__global__ __launch_bounds__(256) void score_kernel(const float *__restrict__ q_pool,
-                                                    const float *__restrict__ k_pool,
-                                                    const float *__restrict__ k_radius,
-                                                    float *__restrict__ P, int hq, int hkv, int nb,
-                                                    float c2) {
-  constexpr int KS = D / 2;  // k-steps; step ks, lane half h <-> dimension ks + KS*h
-  __shared__ float red_m[4][32], red_l[4][32], row_m[32], row_inv[32];
-  __shared__ __attribute__((aligned(16))) float kt_s[4 * 32 * (D + 4)];
-  const int G = (nb + 31) / 32;
-  const int grp = G - 1 - (int)blockIdx.y;
-  const int h = blockIdx.x;
-  const int g = h / (hq / hkv);
-  const int w = threadIdx.x >> 6, lane = threadIdx.x & 63, half = lane >> 5, l32 = lane & 31;
-  const int I0 = grp * 32;
-  const int rows = min(32, nb - I0);
-  const int Il = I0 + l32;  // this lane's query block
-  const bool row_ok = l32 < rows;
-  const int ntc = (I0 + rows - 1) / 32 + 1;  // key-block tiles touching the causal part
-  const bool vec = (nb & 3) == 0;             // rows of P are 16-byte aligned
-  float *pgrp = P + ((size_t)h * nb + I0) * nb;
-
-  // B operand (Qbar^T): lane holds Qbar[Il][ks + KS*half]
-  float qb[KS];
-  {
-    const float *src = q_pool + ((size_t)h * nb + min(Il, nb - 1)) * D + KS * half;
-#pragma unroll
-    for (int i = 0; i < KS; i += 4) {
-      const float4 t = *(const float4 *)(src + i);
-      qb[i] = row_ok ? t.x : 0.f;
-      qb[i + 1] = row_ok ? t.y : 0.f;
-      qb[i + 2] = row_ok ? t.z : 0.f;
-      qb[i + 3] = row_ok ? t.w : 0.f;
-    }
-  }
-  // rescue branch: |Qbar_I| (the lane holds half of the dimensions)
-  float qn = 0.f;
-  if constexpr (RESC) {
-    float ss = 0.f;
-#pragma unroll
-    for (int i = 0; i < KS; ++i) ss = fmaf(qb[i], qb[i], ss);
-    qn = sqrtf(ss + __shfl_xor(ss, 32, 64));
-  }
-  const float *rad = RESC ? k_radius + (size_t)g * nb : nullptr;
-
-  // S^T tile jt: element r of the lane is key block J0 + (r/4)*8 + half*4 + r%4.
-  // The 32 Kbar rows of a tile are one contiguous block: each wave loads it
-  // with coalesced 16-byte loads one tile ahead, stores it to its own padded
-  // LDS slice (row stride D + 4 floats: conflict-free column reads) and reads
-  // the A operand (row l32, dimensions ks + KS*half) back from there.  The
-  // same slice then carries the tile's transpose for row-contiguous stores.
-  constexpr int TF4 = 32 * D / 4 / 64;  // float4 per lane per tile
-  constexpr int RS = D + 4;             // padded LDS row stride (floats)
-  constexpr int TS = 33;                // transpose row stride (floats)
-  float *kt_lds = kt_s + w * 32 * RS;
-  typedef float4 stage_t[TF4];
-  auto fetch = [&](int jt, stage_t &st) {
-    const float *src = k_pool + ((size_t)g * nb + jt * 32) * D;
-    const int n = min(32, nb - jt * 32);
-#pragma unroll
-    for (int i = 0; i < TF4; ++i) {
-      const int f = lane + 64 * i;  // float4 index inside the tile
-      st[i] = f / (D / 4) < n ? *(const float4 *)(src + 4 * f) : make_float4(0.f, 0.f, 0.f, 0.f);
-    }
-  };
-  auto stage = [&](const stage_t &st) {
-#pragma unroll
-    for (int i = 0; i < TF4; ++i) {
-      const int f = lane + 64 * i;
-      *(float4 *)(kt_lds + (f / (D / 4)) * RS + (f % (D / 4)) * 4) = st[i];
-    }
-  };
-  auto mma = [&]() -> f32x16 {
-    const float *arow = kt_lds + l32 * RS + KS * half;
-    float4 a[KS / 4];
-#pragma unroll
-    for (int i = 0; i < KS / 4; ++i) a[i] = *(const float4 *)(arow + 4 * i);
-    f32x16 acc = f32x16{};
-#pragma unroll
-    for (int i = 0; i < KS / 4; ++i) {
-      acc = __builtin_amdgcn_mfma_f32_32x32x2f32(a[i].x, qb[4 * i], acc, 0, 0, 0);
-      acc = __builtin_amdgcn_mfma_f32_32x32x2f32(a[i].y, qb[4 * i + 1], acc, 0, 0, 0);
-      acc = __builtin_amdgcn_mfma_f32_32x32x2f32(a[i].z, qb[4 * i + 2], acc, 0, 0, 0);
-      acc = __builtin_amdgcn_mfma_f32_32x32x2f32(a[i].w, qb[4 * i + 3], acc, 0, 0, 0);
-    }
-    return acc;
-  };
-  // Raw scores of tile jt -> P through the wave's LDS slice: written by
-  // (row, key) = (l32, r), read back so that 8 lanes cover one row's 32 keys.
-  auto put_tile = [&](int jt, const float (&s)[16]) {
-#pragma unroll
-    for (int r = 0; r < 16; ++r) kt_lds[l32 * TS + (r / 4) * 8 + half * 4 + (r % 4)] = s[r];
-    const int c4 = (lane & 7) * 4;
-#pragma unroll
-    for (int it = 0; it < 4; ++it) {
-      const int rr = it * 8 + (lane >> 3);
-      const float *t = kt_lds + rr * TS + c4;
-      const int J = jt * 32 + c4;
-      float *dst = pgrp + (size_t)rr * nb + J;
-      if (rr < rows) {
-        if (vec && J + 3 < nb) {
-          *(float4 *)dst = make_float4(t[0], t[1], t[2], t[3]);
-        } else {
-#pragma unroll
-          for (int e = 0; e < 4; ++e)
-            if (J + e < nb) dst[e] = t[e];
-        }
-      }
-    }
-  };
-
-  // ---- pass 1: raw log2-domain scores to P, row max and sum of exp2
-  float m = -INFINITY, l = 0.f;
-  stage_t nxt;
-  if (w < ntc) fetch(w, nxt);
-  for (int jt = w; jt < ntc; jt += 4) {
-    stage(nxt);
-    if (jt + 4 < ntc) fetch(jt + 4, nxt);
-    const f32x16 acc = mma();
-    float s[16];
-    float tmax = -INFINITY;
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int J = jt * 32 + (r / 4) * 8 + half * 4 + (r % 4);
-      const float add = RESC && J < nb ? qn * rad[J] : 0.f;
-      s[r] = (J <= Il && J < nb) ? (acc[r] + add) * c2 : -INFINITY;
-      tmax = fmaxf(tmax, s[r]);
-    }
-    put_tile(jt, s);
-    const float mn = fmaxf(m, tmax);
-    if (mn != -INFINITY) {
-      float acc_l = 0.f;
-#pragma unroll
-      for (int r = 0; r < 16; ++r) acc_l += exp2f(s[r] - mn);
-      l = l * exp2f(m - mn) + acc_l;
-      m = mn;
-    }
-  }
-  // merge the two lane halves, then the four wavefronts
-  {
-    const float mo = __shfl_xor(m, 32, 64), lo = __shfl_xor(l, 32, 64);
-    const float mn = fmaxf(m, mo);
-    if (mn != -INFINITY) {
-      l = (m == -INFINITY ? 0.f : l * exp2f(m - mn)) + (mo == -INFINITY ? 0.f : lo * exp2f(mo - mn));
-      m = mn;
-    }
-  }
-  if (half == 0) {
-    red_m[w][l32] = m;
-    red_l[w][l32] = l;
-  }
-  __syncthreads();
-  if (w == 0 && half == 0) {
-    float M = -INFINITY;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) M = fmaxf(M, red_m[i][l32]);
-    float L = 0.f;
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-      if (red_m[i][l32] != -INFINITY) L += red_l[i][l32] * exp2f(red_m[i][l32] - M);
-    row_m[l32] = M;
-    row_inv[l32] = L > 0.f ? 1.f / L : 0.f;
-  }
-  __syncthreads();
-
-  // ---- pass 2: the group's rows of P, row-major and coalesced: causal
-  // entries become exp2(s - M) / L from the raw scores of pass 1, the rest 0.
-  const int jend = ntc * 32;  // raw scores exist for J < jend (-inf above the diagonal)
-  if (vec) {
-    // 8 rows per batch: all loads are issued before the first store
-    for (int J = threadIdx.x * 4; J < nb; J += 1024) {
-      for (int r0 = 0; r0 < rows; r0 += 8) {
-        float4 v[8];
-#pragma unroll
-        for (int u = 0; u < 8; ++u) {
-          const int rr = r0 + u;
-          v[u] = (rr < rows && J < jend) ? *(const float4 *)(pgrp + (size_t)rr * nb + J)
-                                         : make_float4(0.f, 0.f, 0.f, 0.f);
-        }
-#pragma unroll
-        for (int u = 0; u < 8; ++u) {
-          const int rr = r0 + u;
-          if (rr < rows) {
-            if (J < jend) {
-              const float M = row_m[rr], inv = row_inv[rr];
-              v[u].x = exp2f(v[u].x - M) * inv;
-              v[u].y = exp2f(v[u].y - M) * inv;
-              v[u].z = exp2f(v[u].z - M) * inv;
-              v[u].w = exp2f(v[u].w - M) * inv;
-            }
-            *(float4 *)(pgrp + (size_t)rr * nb + J) = v[u];
-          }
-        }
-      }
-    }
-  } else {
-    for (int rr = 0; rr < rows; ++rr) {
-      const float M = row_m[rr], inv = row_inv[rr];
-      float *prow = pgrp + (size_t)rr * nb;
-      for (int J = threadIdx.x; J < nb; J += 256)
-        prow[J] = J < jend ? exp2f(prow[J] - M) * inv : 0.f;
-    }
-  }
-}
 
 // Rows of at most 1024 key blocks: eight wavefronts split the key-block tiles
 // of the group (at most four each) and keep their raw scores in registers,
@@ -504,6 +298,204 @@ __global__ __launch_bounds__(512) void score_kernel_reg(const float *__restrict_
   }
 }
 
+// Rows longer than 1024 blocks: the same split-plane products and Kbar
+// staging as score_kernel_reg, but nothing is held across tiles.  Pass 1
+// computes the row statistics only; pass 2 recomputes every tile and writes
+// P once, normalised, straight from the MFMA layout (lane (l32, half) owns
+// row I0 + l32 and four runs of 4 consecutive key blocks per tile).  The
+// stores of a tile are issued after the next half's loads, so the wait for
+// those loads does not also wait for them at once.  Any row length.
+template <int D, bool RESC>
+__global__ __launch_bounds__(512) void score_kernel_2p(const float *__restrict__ q_pool,
+                                                       const float *__restrict__ k_pool,
+                                                       const float *__restrict__ k_radius,
+                                                       float *__restrict__ P, int hq, int hkv,
+                                                       int nb, float c2) {
+  using S = ScoreStage<D>;
+  constexpr int NWV = 8;      // wavefronts
+  constexpr int NS = D / 16;  // MFMA steps per tile (16 dimensions each)
+  constexpr int CPR = S::CPR, NDMA = S::NDMA;
+  __shared__ float red_m[NWV][32], red_l[NWV][32], row_m[32], row_inv[32];
+  __shared__ __attribute__((aligned(16))) uint8_t stg0[NWV][S::HB];
+  __shared__ __attribute__((aligned(16))) uint8_t stg1[NWV][S::HB];
+  const int G = (nb + 31) / 32;
+  const int grp = G - 1 - (int)blockIdx.y;
+  const int h = blockIdx.x;
+  const int g = h / (hq / hkv);
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63, half = lane >> 5, l32 = lane & 31;
+  const int I0 = grp * 32;
+  const int rows = min(32, nb - I0);
+  const int Il = I0 + l32;  // this lane's query block
+  const bool row_ok = l32 < rows;
+  const int ntc = (I0 + rows - 1) / 32 + 1;              // key-block tiles touching the causal part
+  const int nt = w < ntc ? (ntc - w + NWV - 1) / NWV : 0;  // this wave's tiles: w, w + 8, ...
+  const bool vec = (nb & 3) == 0;                         // rows of P are 16-byte aligned
+  float *prow = P + ((size_t)h * nb + min(Il, nb - 1)) * nb;
+
+  int vrow[NDMA];        // source row of each load
+  uint32_t vdim[NDMA];   // its byte offset inside the row
+#pragma unroll
+  for (int it = 0; it < NDMA; ++it) {
+    const int p = it * 64 + lane, c = p % (CPR + 1);
+    const int cc = c < CPR ? c : 0;
+    const int kg = cc / (CPR / 2), rem = cc % (CPR / 2);
+    vrow[it] = min(p / (CPR + 1), 31);
+    vdim[it] = (uint32_t)((D / 2) * kg + 4 * rem) * 4;
+  }
+  const __amdgpu_buffer_rsrc_t krs =
+      make_rsrc(k_pool + (size_t)g * nb * D, (uint32_t)((size_t)nb * D * 4));
+  // unit U (0 <= U < 4 nt) = half U % 2 of the wave's tile (U / 2) % nt: pass
+  // 1 takes units 0 .. 2nt - 1, pass 2 the rest, into buffer U % 2
+  auto issue = [&](int U) {
+    const int jt = w + NWV * ((U >> 1) % nt);
+    const uint32_t soff = (uint32_t)(jt * 32 * D + (U & 1) * (D / 4)) * 4;
+    uint8_t *dst = (U & 1) ? &stg1[w][0] : &stg0[w][0];
+    const int last = nb - 1 - jt * 32;
+#pragma unroll
+    for (int it = 0; it < NDMA; ++it)
+      lds_dma16(krs, (uint32_t)min(vrow[it], last) * (D * 4) + vdim[it], soff, dst + it * 1024);
+  };
+  if (nt > 0) issue(0);
+
+  bf16x8 qh[NS], qm[NS], ql[NS];
+  float qn = 0.f;  // rescue branch: |Qbar_I|
+  {
+    const float *src = q_pool + ((size_t)h * nb + min(Il, nb - 1)) * D + (D / 2) * half;
+    float ss = 0.f;
+#pragma unroll
+    for (int s = 0; s < NS; ++s) {
+      const float4 t0 = *(const float4 *)(src + 8 * s), t1 = *(const float4 *)(src + 8 * s + 4);
+      float x[8] = {t0.x, t0.y, t0.z, t0.w, t1.x, t1.y, t1.z, t1.w};
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        x[e] = row_ok ? x[e] : 0.f;
+        if constexpr (RESC) ss = fmaf(x[e], x[e], ss);
+      }
+      split3(x, qh[s], qm[s], ql[s]);
+    }
+    if constexpr (RESC) qn = sqrtf(ss + __shfl_xor(ss, 32, 64));
+  }
+  const float *rad = RESC ? k_radius + (size_t)g * nb : nullptr;
+
+  // log2-domain scores of the wave's tile t (units U0, U0 + 1); `between`
+  // runs after the second half's loads are issued
+  auto tile = [&](int t, int U0, float (&x)[16], auto between) {
+    const int jt = w + NWV * t;
+    f32x16 big = f32x16{}, small = f32x16{};
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh) {
+      const int U = U0 + hh;
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      issue(U + 1 < 4 * nt ? U + 1 : U - 1);  // the last unit repeats one, never read
+      if (hh == 1) between();
+      __builtin_amdgcn_sched_barrier(0);
+      score_half<D, RESC>(hh ? &stg1[w][0] : &stg0[w][0], hh, half, l32, qh, qm, ql, big, small);
+    }
+    const bool edge = jt * 32 + 31 > I0 || jt * 32 + 31 >= nb;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int J = jt * 32 + (r / 4) * 8 + half * 4 + (r % 4);
+      const float add = RESC && J < nb ? qn * rad[J] : 0.f;
+      const float v = (big[r] + small[r] + add) * c2;
+      x[r] = (!edge || (J <= Il && J < nb)) ? v : -INFINITY;
+    }
+  };
+
+  // ---- pass 1: row max and sum of exp2
+  float m = -INFINITY, l = 0.f;
+  for (int t = 0; t < nt; ++t) {
+    float x[16];
+    tile(t, 2 * t, x, [] {});
+    float tmax = -INFINITY;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) tmax = fmaxf(tmax, x[r]);
+    const float mn = fmaxf(m, tmax);
+    if (mn != -INFINITY) {
+      float acc_l = 0.f;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc_l += __builtin_amdgcn_exp2f(x[r] - mn);
+      l = l * __builtin_amdgcn_exp2f(m - mn) + acc_l;
+      m = mn;
+    }
+  }
+  {
+    const float mo = __shfl_xor(m, 32, 64), lo = __shfl_xor(l, 32, 64);
+    const float mn = fmaxf(m, mo);
+    if (mn != -INFINITY) {
+      l = (m == -INFINITY ? 0.f : l * __builtin_amdgcn_exp2f(m - mn)) +
+          (mo == -INFINITY ? 0.f : lo * __builtin_amdgcn_exp2f(mo - mn));
+      m = mn;
+    }
+  }
+  if (half == 0) {
+    red_m[w][l32] = m;
+    red_l[w][l32] = l;
+  }
+  __syncthreads();
+  if (w == 0 && half == 0) {
+    float M = -INFINITY;
+#pragma unroll
+    for (int i = 0; i < NWV; ++i) M = fmaxf(M, red_m[i][l32]);
+    float L = 0.f;
+#pragma unroll
+    for (int i = 0; i < NWV; ++i)
+      if (red_m[i][l32] != -INFINITY)
+        L += red_l[i][l32] * __builtin_amdgcn_exp2f(red_m[i][l32] - M);
+    row_m[l32] = M;
+    row_inv[l32] = L > 0.f ? 1.f / L : 0.f;
+  }
+  __syncthreads();
+
+  // ---- pass 2: recompute each tile, write P normalised; a tile's stores go
+  // out during the next tile
+  const float M = row_m[l32], inv = row_inv[l32];
+  float pv[16];
+  int pjt = -1;  // tile whose values pv holds
+  auto store = [&]() {
+    if (pjt < 0 || !row_ok) return;
+#pragma unroll
+    for (int q4 = 0; q4 < 4; ++q4) {
+      const int J = pjt * 32 + q4 * 8 + half * 4;
+      if (vec && J + 3 < nb) {
+        *(float4 *)(prow + J) =
+            make_float4(pv[4 * q4], pv[4 * q4 + 1], pv[4 * q4 + 2], pv[4 * q4 + 3]);
+      } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          if (J + e < nb) prow[J + e] = pv[4 * q4 + e];
+      }
+    }
+  };
+  for (int t = 0; t < nt; ++t) {
+    float x[16];
+    tile(t, 2 * nt + 2 * t, x, store);
+#pragma unroll
+    for (int r = 0; r < 16; ++r) pv[r] = __builtin_amdgcn_exp2f(x[r] - M) * inv;
+    pjt = w + NWV * t;
+  }
+  store();
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // the repeat load has landed before exit
+  // zeros above the causal tiles, all threads, row-major
+  float *pgrp = P + ((size_t)h * nb + I0) * nb;
+  const int jend = ntc * 32;
+  if (jend < nb) {
+    if (vec) {
+      const int n4 = (nb - jend) / 4;
+      for (int e = threadIdx.x; e < rows * n4; e += 512) {
+        const int rr = e / n4, J = jend + (e - rr * n4) * 4;
+        *(float4 *)(pgrp + (size_t)rr * nb + J) = make_float4(0.f, 0.f, 0.f, 0.f);
+      }
+    } else {
+      const int n1 = nb - jend;
+      for (int e = threadIdx.x; e < rows * n1; e += 512) {
+        const int rr = e / n1;
+        pgrp[(size_t)rr * nb + jend + (e - rr * n1)] = 0.f;
+      }
+    }
+  }
+}
+
 template <int D, bool RESC>
 static hipError_t launch_score_t(const Shape &s, float c, const float *qp, const float *kp,
                                  const float *kr, float *S, hipStream_t st) {
@@ -513,7 +505,7 @@ static hipError_t launch_score_t(const Shape &s, float c, const float *qp, const
     hipLaunchKernelGGL((score_kernel_reg<D, RESC>), grid, dim3(512), 0, st, qp, kp, kr, S, s.hq,
                        s.hkv, s.nb, c * kLog2e);
   else
-    hipLaunchKernelGGL((score_kernel<D, RESC>), grid, dim3(256), 0, st, qp, kp, kr, S, s.hq,
+    hipLaunchKernelGGL((score_kernel_2p<D, RESC>), grid, dim3(512), 0, st, qp, kp, kr, S, s.hq,
                        s.hkv, s.nb, c * kLog2e);
   return hipGetLastError();
 }

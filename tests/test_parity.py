@@ -229,10 +229,11 @@ def _pooled_accuracy_case(which):
 
 
 @pytest.mark.parametrize("which", ["f32_64_64_100", "bf16_128_128_70", "fp8_128_128_45",
-                                   "bf16_64_128_130"])
+                                   "bf16_64_128_130", "bf16_64_64_1100", "fp8_128_128_1030"])
 @pytest.mark.parametrize("rescue", [False, True])
 def test_pooled_scores_at_fp32_accuracy(which, rescue):
-    """The pooled scores are as accurate as fp32 dot products.
+    """The pooled scores are as accurate as fp32 dot products (rows of up to
+    1024 blocks and longer ones, which take the other score kernel).
 
     Where P is at least 1e-6 of its row maximum, log P is within
     2e-6 + 2^-20 * c * sum_i |Qbar_i Kbar_i| of the fp64 oracle: the size of
