@@ -27,6 +27,9 @@
  *     a kernel surface at the caller's next synchronisation.
  *   - Layouts are row-major and contiguous: Q [hq][seq][d], K and V
  *     [hkv][seq][d].  q head h reads kv head h / (hq / hkv) (GQA).
+ *   - Base pointers are expected to be 16-byte aligned, as hipMalloc and
+ *     torch allocations are: the kernels move data in 16-byte vectors
+ *     wherever the row strides keep them aligned.
  *   - nb = ceil(seq / block).  A last block shorter than `block` holds the
  *     seq % block tail tokens; it pools over those tokens only.
  *   - seq == 0 is valid and does nothing (after the descriptor checks; the
