@@ -4,13 +4,15 @@
 // Appendix B: query tiles against causally valid pooled key blocks, then a
 // global normalisation).
 //
-// Two passes over the causal block grid of a group of 32 query blocks:
+// One workgroup per group of 32 query blocks of a head, in two passes:
 //   pass 1  S^T tiles = Kbar Qbar^T (32 key blocks x 32 query blocks), with
 //           fp32-accurate products and sums so that the threshold downstream
-//           sees full-precision scores, reduced to the running row max and
+//           sees full-precision scores, each computed once: its raw
+//           log2-domain scores go to P, its rows into the running max and
 //           sum of exp;
-//   pass 2  after the row statistics meet, P = exp(S - max) / sum on the
-//           causal part, zeros above it.
+//   pass 2  after the row statistics meet, the workgroup rewrites its rows
+//           of P in place, P = exp(S - max) / sum on the causal part, zeros
+//           above it.
 // Each lane owns one query block (a column of S^T), so the row reductions are
 // in-lane plus one exchange with the lane 32 away; the wavefronts of a
 // workgroup split the key-block tiles of the same 32 query blocks and merge
@@ -18,25 +20,15 @@
 // groups of every head first.
 //
 // With a key-block radius r (rescue branch, thelatestinai page, RBS-Attention
-// abstract) the same kernels compute c (Qbar_I . Kbar_J + |Qbar_I| r_J), an
+// abstract) the same kernel computes c (Qbar_I . Kbar_J + |Qbar_I| r_J), an
 // upper bound on the block's best per-key logit, and its row softmax.
-//
-// Both kernels form the products on bf16 matrix cores over three bf16 planes
-// of each operand.  score_kernel_reg (rows of at most 1024 blocks): eight
-// wavefronts with at most four tiles each keep their raw scores in
-// registers, so P is written once, normalised, through an LDS transpose that
-// makes every store cover whole 128-byte row runs.  score_kernel_2p (longer
-// rows): pass 2 recomputes the tiles instead of holding them, and writes P
-// once from the MFMA layout.
 #include "device.h"
 #include "internal.h"
 
 namespace bsp {
 
-// Rows of at most 1024 key blocks: eight wavefronts split the key-block tiles
-// of the group (at most four each) and keep their raw scores in registers,
-// so P is written once, already normalised, and never read back.
-//
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
 // The dot products run on v_mfma_f32_32x32x16_bf16 over three bf16 planes of
 // each operand: hi*hi + hi*mid + mid*hi + hi*lo + lo*hi + mid*mid leaves out
 // only terms below 2^-24 of each product, every plane product is exact and
@@ -92,227 +84,24 @@ __device__ __forceinline__ void score_half(const uint8_t *__restrict__ buf, int 
   }
 }
 
-template <int D, bool RESC>
-__global__ __launch_bounds__(512) void score_kernel_reg(const float *__restrict__ q_pool,
-                                                        const float *__restrict__ k_pool,
-                                                        const float *__restrict__ k_radius,
-                                                        float *__restrict__ P, int hq, int hkv,
-                                                        int nb, float c2) {
-  using S = ScoreStage<D>;
-  constexpr int NWV = 8;      // wavefronts
-  constexpr int MAXT = 4;     // tiles per wavefront
-  constexpr int NS = D / 16;  // MFMA steps per tile (16 dimensions each)
-  constexpr int CPR = S::CPR, NDMA = S::NDMA;
-  static_assert(S::HB >= 32 * 33 * 4, "the pass-2 transpose reuses a half buffer");
-  __shared__ float red_m[NWV][32], red_l[NWV][32], row_m[32], row_inv[32];
-  // one array per half, so the compiler sees that a load into one half
-  // cannot alias reads of the other and does not wait for it
-  __shared__ __attribute__((aligned(16))) uint8_t stg0[NWV][S::HB];
-  __shared__ __attribute__((aligned(16))) uint8_t stg1[NWV][S::HB];
-  const int G = (nb + 31) / 32;
-  const int grp = G - 1 - (int)blockIdx.y;
-  const int h = blockIdx.x;
-  const int g = h / (hq / hkv);
-  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int lane = threadIdx.x & 63, half = lane >> 5, l32 = lane & 31;
-  const int I0 = grp * 32;
-  const int rows = min(32, nb - I0);
-  const int Il = I0 + l32;  // this lane's query block
-  const bool row_ok = l32 < rows;
-  const int ntc = (I0 + rows - 1) / 32 + 1;  // key-block tiles touching the causal part
-  const int nt = w < ntc ? min(MAXT, (ntc - w + NWV - 1) / NWV) : 0;  // this wave's tiles
-  const bool vec = (nb & 3) == 0;             // rows of P are 16-byte aligned
-  float *pgrp = P + ((size_t)h * nb + I0) * nb;
-
-  // direct-to-LDS staging: load it of a half puts the lane's 16 bytes at
-  // position it * 64 + lane = row * (CPR + 1) + chunk of the wavefront's
-  // buffer; the padding chunk and the positions past row 31 take a copy of
-  // an in-bounds chunk that is never read
-  const __amdgpu_buffer_rsrc_t krs =
-      make_rsrc(k_pool + (size_t)g * nb * D, (uint32_t)((size_t)nb * D * 4));
-  int vrow[NDMA];        // source row of each load
-  uint32_t vdim[NDMA];   // its byte offset inside the row
-#pragma unroll
-  for (int it = 0; it < NDMA; ++it) {
-    const int p = it * 64 + lane, c = p % (CPR + 1);
-    const int cc = c < CPR ? c : 0;
-    const int kg = cc / (CPR / 2), rem = cc % (CPR / 2);
-    vrow[it] = min(p / (CPR + 1), 31);
-    vdim[it] = (uint32_t)((D / 2) * kg + 4 * rem) * 4;
-  }
-  // unit u = half u % 2 of the wavefront's tile u / 2 (key blocks jt*32 ..)
-  // into buffer u % 2.  Rows past the last key block re-read it (a clamp,
-  // not a branch: the compiler's wait tracking then sees every load in
-  // flight and lets the reads of the other buffer go ahead).
-  auto issue = [&](int u) {
-    const int jt = w + NWV * (u >> 1);
-    const uint32_t soff = (uint32_t)(jt * 32 * D + (u & 1) * (D / 4)) * 4;
-    uint8_t *dst = (u & 1) ? &stg1[w][0] : &stg0[w][0];
-    const int last = nb - 1 - jt * 32;
-#pragma unroll
-    for (int it = 0; it < NDMA; ++it)
-      lds_dma16(krs, (uint32_t)min(vrow[it], last) * (D * 4) + vdim[it], soff, dst + it * 1024);
-  };
-  // the first Kbar half goes out before the Qbar loads, so the two latencies overlap
-  if (nt > 0) issue(0);
-
-  // B operand (Qbar^T) planes: lane (n, kg) holds Qbar[I0 + n] at dimensions
-  // D/2*kg + 8s .. + 8 for step s
-  bf16x8 qh[NS], qm[NS], ql[NS];
-  float qn = 0.f;  // rescue branch: |Qbar_I|
-  {
-    const float *src = q_pool + ((size_t)h * nb + min(Il, nb - 1)) * D + (D / 2) * half;
-    float ss = 0.f;
-#pragma unroll
-    for (int s = 0; s < NS; ++s) {
-      const float4 t0 = *(const float4 *)(src + 8 * s), t1 = *(const float4 *)(src + 8 * s + 4);
-      float x[8] = {t0.x, t0.y, t0.z, t0.w, t1.x, t1.y, t1.z, t1.w};
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        x[e] = row_ok ? x[e] : 0.f;
-        if constexpr (RESC) ss = fmaf(x[e], x[e], ss);
-      }
-      split3(x, qh[s], qm[s], ql[s]);
-    }
-    if constexpr (RESC) qn = sqrtf(ss + __shfl_xor(ss, 32, 64));
-  }
-  const float *rad = RESC ? k_radius + (size_t)g * nb : nullptr;
-
-  // ---- pass 1: raw log2-domain scores held in registers, row max and sum
-  float held[MAXT][16];
-  float m = -INFINITY, l = 0.f;
-#pragma unroll
-  for (int t = 0; t < MAXT; ++t) {
-    if (t < nt) {
-      const int jt = w + NWV * t;
-      f32x16 big = f32x16{}, small = f32x16{};
-#pragma unroll
-      for (int hh = 0; hh < 2; ++hh) {
-        const int u = 2 * t + hh;
-        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-        // after the last unit the idle buffer takes a repeat of unit u - 1
-        // (never read): every unit issues exactly one load group
-        issue(u + 1 < 2 * nt ? u + 1 : u - 1);
-        __builtin_amdgcn_sched_barrier(0);  // the loads go out before the MFMAs
-        score_half<D, RESC>(hh ? &stg1[w][0] : &stg0[w][0], hh, half, l32, qh, qm, ql, big, small);
-      }
-      // only the diagonal tile (and a ragged last one) has entries to mask
-      const bool edge = jt * 32 + 31 > I0 || jt * 32 + 31 >= nb;
-      float tmax = -INFINITY;
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int J = jt * 32 + (r / 4) * 8 + half * 4 + (r % 4);
-        const float add = RESC && J < nb ? qn * rad[J] : 0.f;
-        const float x = (big[r] + small[r] + add) * c2;
-        held[t][r] = (!edge || (J <= Il && J < nb)) ? x : -INFINITY;
-        tmax = fmaxf(tmax, held[t][r]);
-      }
-      const float mn = fmaxf(m, tmax);
-      if (mn != -INFINITY) {
-        float acc_l = 0.f;
-#pragma unroll
-        for (int r = 0; r < 16; ++r) acc_l += __builtin_amdgcn_exp2f(held[t][r] - mn);
-        l = l * __builtin_amdgcn_exp2f(m - mn) + acc_l;
-        m = mn;
-      }
-    }
-  }
-  {
-    const float mo = __shfl_xor(m, 32, 64), lo = __shfl_xor(l, 32, 64);
-    const float mn = fmaxf(m, mo);
-    if (mn != -INFINITY) {
-      l = (m == -INFINITY ? 0.f : l * __builtin_amdgcn_exp2f(m - mn)) +
-          (mo == -INFINITY ? 0.f : lo * __builtin_amdgcn_exp2f(mo - mn));
-      m = mn;
-    }
-  }
-  if (half == 0) {
-    red_m[w][l32] = m;
-    red_l[w][l32] = l;
-  }
-  __syncthreads();
-  if (w == 0 && half == 0) {
-    float M = -INFINITY;
-#pragma unroll
-    for (int i = 0; i < NWV; ++i) M = fmaxf(M, red_m[i][l32]);
-    float L = 0.f;
-#pragma unroll
-    for (int i = 0; i < NWV; ++i)
-      if (red_m[i][l32] != -INFINITY)
-        L += red_l[i][l32] * __builtin_amdgcn_exp2f(red_m[i][l32] - M);
-    row_m[l32] = M;
-    row_inv[l32] = L > 0.f ? 1.f / L : 0.f;
-  }
-  __syncthreads();
-
-  // ---- pass 2: normalise the held tiles and write them through the wave's
-  // LDS slice, so that 8 lanes cover one row's 32 keys of a tile
-  {
-    constexpr int TS = 33;  // transpose row stride (floats)
-    float *kt_lds = (float *)&stg0[w][0];
-    const float M = row_m[l32], inv = row_inv[l32];
-    const int c4 = (lane & 7) * 4;
-#pragma unroll
-    for (int t = 0; t < MAXT; ++t) {
-      const int jt = w + t * NWV;
-      if (t < nt) {
-#pragma unroll
-        for (int r = 0; r < 16; ++r)
-          kt_lds[l32 * TS + (r / 4) * 8 + half * 4 + (r % 4)] =
-              __builtin_amdgcn_exp2f(held[t][r] - M) * inv;
-#pragma unroll
-        for (int it = 0; it < 4; ++it) {
-          const int rr = it * 8 + (lane >> 3);
-          const float *tp = kt_lds + rr * TS + c4;
-          const int J = jt * 32 + c4;
-          float *dst = pgrp + (size_t)rr * nb + J;
-          if (rr < rows) {
-            if (vec && J + 3 < nb) {
-              *(float4 *)dst = make_float4(tp[0], tp[1], tp[2], tp[3]);
-            } else {
-#pragma unroll
-              for (int e = 0; e < 4; ++e)
-                if (J + e < nb) dst[e] = tp[e];
-            }
-          }
-        }
-      }
-    }
-  }
-  // zeros above the causal tiles, all threads, row-major
-  const int jend = ntc * 32;
-  if (jend < nb) {
-    if (vec) {
-      const int n4 = (nb - jend) / 4;
-      for (int e = threadIdx.x; e < rows * n4; e += 512) {
-        const int rr = e / n4, J = jend + (e - rr * n4) * 4;
-        *(float4 *)(pgrp + (size_t)rr * nb + J) = make_float4(0.f, 0.f, 0.f, 0.f);
-      }
-    } else {
-      const int n1 = nb - jend;
-      for (int e = threadIdx.x; e < rows * n1; e += 512) {
-        const int rr = e / n1;
-        pgrp[(size_t)rr * nb + jend + (e - rr * n1)] = 0.f;
-      }
-    }
-  }
-}
-
-// Rows longer than 1024 blocks: the same split-plane products and Kbar
-// staging as score_kernel_reg, but nothing is held across tiles.  Pass 1
-// computes the row statistics only; pass 2 recomputes every tile and writes
-// P once, normalised, straight from the MFMA layout (lane (l32, half) owns
-// row I0 + l32 and four runs of 4 consecutive key blocks per tile).  The
-// stores of a tile are issued after the next half's loads, so the wait for
-// those loads does not also wait for them at once.  Any row length.
-template <int D, bool RESC>
-__global__ __launch_bounds__(512) void score_kernel_2p(const float *__restrict__ q_pool,
+// Any row length.  Pass 1 computes each tile once and stores its raw
+// log2-domain scores into P while the row statistics accumulate; after the
+// statistics meet, the workgroup rewrites its rows in place, normalised,
+// with row-major 16-byte loads and stores, and fills the zeros above.  The
+// rewrite reads back what pass 1 just wrote (mostly from the caches) instead
+// of recomputing the products: at 2048 blocks per row a recomputing pass 2
+// cost as much as pass 1.  Four wavefronts (72 KiB of staging) let two
+// workgroups share a CU, so one's loads, barriers and stores overlap the
+// other's products.
+template <int D, bool RESC, bool VEC>
+__global__ __launch_bounds__(256, 2) void score_kernel(const float *__restrict__ q_pool,
                                                        const float *__restrict__ k_pool,
                                                        const float *__restrict__ k_radius,
                                                        float *__restrict__ P, int hq, int hkv,
                                                        int nb, float c2) {
   using S = ScoreStage<D>;
-  constexpr int NWV = 8;      // wavefronts
+  constexpr int NWV = 4;      // wavefronts
+  constexpr int NT = NWV * 64;
   constexpr int NS = D / 16;  // MFMA steps per tile (16 dimensions each)
   constexpr int CPR = S::CPR, NDMA = S::NDMA;
   __shared__ float red_m[NWV][32], red_l[NWV][32], row_m[32], row_inv[32];
@@ -329,9 +118,9 @@ __global__ __launch_bounds__(512) void score_kernel_2p(const float *__restrict__
   const int Il = I0 + l32;  // this lane's query block
   const bool row_ok = l32 < rows;
   const int ntc = (I0 + rows - 1) / 32 + 1;              // key-block tiles touching the causal part
-  const int nt = w < ntc ? (ntc - w + NWV - 1) / NWV : 0;  // this wave's tiles: w, w + 8, ...
-  const bool vec = (nb & 3) == 0;                         // rows of P are 16-byte aligned
-  float *prow = P + ((size_t)h * nb + min(Il, nb - 1)) * nb;
+  const int nt = w < ntc ? (ntc - w + NWV - 1) / NWV : 0;  // this wave's tiles: w, w + NWV, ...
+  constexpr bool vec = VEC;  // nb % 4 == 0: rows of P are 16-byte aligned
+  float *pgrp = P + ((size_t)h * nb + I0) * nb;
 
   int vrow[NDMA];        // source row of each load
   uint32_t vdim[NDMA];   // its byte offset inside the row
@@ -345,10 +134,9 @@ __global__ __launch_bounds__(512) void score_kernel_2p(const float *__restrict__
   }
   const __amdgpu_buffer_rsrc_t krs =
       make_rsrc(k_pool + (size_t)g * nb * D, (uint32_t)((size_t)nb * D * 4));
-  // unit U (0 <= U < 4 nt) = half U % 2 of the wave's tile (U / 2) % nt: pass
-  // 1 takes units 0 .. 2nt - 1, pass 2 the rest, into buffer U % 2
+  // unit U (0 <= U < 2 nt) = half U % 2 of the wave's tile U / 2, into buffer U % 2
   auto issue = [&](int U) {
-    const int jt = w + NWV * ((U >> 1) % nt);
+    const int jt = w + NWV * (U >> 1);
     const uint32_t soff = (uint32_t)(jt * 32 * D + (U & 1) * (D / 4)) * 4;
     uint8_t *dst = (U & 1) ? &stg1[w][0] : &stg0[w][0];
     const int last = nb - 1 - jt * 32;
@@ -378,47 +166,93 @@ __global__ __launch_bounds__(512) void score_kernel_2p(const float *__restrict__
   }
   const float *rad = RESC ? k_radius + (size_t)g * nb : nullptr;
 
-  // log2-domain scores of the wave's tile t (units U0, U0 + 1); `between`
-  // runs after the second half's loads are issued
-  auto tile = [&](int t, int U0, float (&x)[16], auto between) {
+  // ---- pass 1: each tile once; raw scores to P (a tile's stores go out
+  // during the next tile), row max and sum of exp2
+  float m = -INFINITY, l = 0.f;
+  float pv[16];
+  int pjt = -1;  // tile whose raw scores pv holds
+  // The stores are buffer stores, the same number on every call (4, or 16
+  // for rows that are not 16-byte aligned): lanes without scores to write
+  // drop out through the buffer's range check.  With no branch around them
+  // the compiler's own waits before the next half's LDS reads count them
+  // exactly and do not also wait for the loads issued before them.
+  const __amdgpu_buffer_rsrc_t prs = make_rsrc(pgrp, (uint32_t)((size_t)rows * nb * 4));
+  constexpr uint32_t kDrop = 0x80000000u;  // past any range
+  auto store = [&]() {
+    const bool ok = pjt >= 0 && row_ok;
+    const uint32_t rb = (uint32_t)(l32 * nb) * 4;
+#pragma unroll
+    for (int q4 = 0; q4 < 4; ++q4) {
+      const int J = pjt * 32 + q4 * 8 + half * 4;
+      if constexpr (VEC) {
+        const u32x4 v = {__float_as_uint(pv[4 * q4]), __float_as_uint(pv[4 * q4 + 1]),
+                         __float_as_uint(pv[4 * q4 + 2]), __float_as_uint(pv[4 * q4 + 3])};
+        __builtin_amdgcn_raw_buffer_store_b128(v, prs, ok && J < nb ? rb + J * 4 : kDrop, 0, 0);
+      } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(pv[4 * q4 + e]), prs,
+                                                ok && J + e < nb ? rb + (J + e) * 4 : kDrop, 0, 0);
+      }
+    }
+  };
+  // rescue branch: the tile's key radii, loaded ahead of the next unit's
+  // Kbar (the waits are in issue order, so a load issued after it and used
+  // at once would also wait for the Kbar)
+  float rv[RESC ? 16 : 1];
+  auto load_rad = [&](int jt) {
+#pragma unroll
+    for (int q4 = 0; q4 < 4; ++q4) {
+      const int J = jt * 32 + q4 * 8 + half * 4;
+      if (vec && J < nb) {
+        const float4 t4 = *(const float4 *)(rad + J);
+        rv[4 * q4] = t4.x; rv[4 * q4 + 1] = t4.y; rv[4 * q4 + 2] = t4.z; rv[4 * q4 + 3] = t4.w;
+      } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) rv[4 * q4 + e] = J + e < nb ? rad[J + e] : 0.f;
+      }
+    }
+  };
+  for (int t = 0; t < nt; ++t) {
     const int jt = w + NWV * t;
     f32x16 big = f32x16{}, small = f32x16{};
 #pragma unroll
     for (int hh = 0; hh < 2; ++hh) {
-      const int U = U0 + hh;
+      const int U = 2 * t + hh;
+      // the previous half's products stay ahead of this wait (the compiler
+      // would otherwise sink some of them past it, shortening the time the
+      // loads in flight have to land)
+      __builtin_amdgcn_sched_barrier(0);
       asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-      issue(U + 1 < 4 * nt ? U + 1 : U - 1);  // the last unit repeats one, never read
-      if (hh == 1) between();
+      if constexpr (RESC)
+        if (hh == 0) load_rad(jt);
+      issue(U + 1 < 2 * nt ? U + 1 : U - 1);  // the last unit repeats one, never read
+      if (hh == 1) store();
       __builtin_amdgcn_sched_barrier(0);
       score_half<D, RESC>(hh ? &stg1[w][0] : &stg0[w][0], hh, half, l32, qh, qm, ql, big, small);
     }
     const bool edge = jt * 32 + 31 > I0 || jt * 32 + 31 >= nb;
+    float tmax = -INFINITY;
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       const int J = jt * 32 + (r / 4) * 8 + half * 4 + (r % 4);
-      const float add = RESC && J < nb ? qn * rad[J] : 0.f;
+      const float add = RESC && J < nb ? qn * rv[RESC ? r : 0] : 0.f;
       const float v = (big[r] + small[r] + add) * c2;
-      x[r] = (!edge || (J <= Il && J < nb)) ? v : -INFINITY;
+      pv[r] = (!edge || (J <= Il && J < nb)) ? v : -INFINITY;
+      tmax = fmaxf(tmax, pv[r]);
     }
-  };
-
-  // ---- pass 1: row max and sum of exp2
-  float m = -INFINITY, l = 0.f;
-  for (int t = 0; t < nt; ++t) {
-    float x[16];
-    tile(t, 2 * t, x, [] {});
-    float tmax = -INFINITY;
-#pragma unroll
-    for (int r = 0; r < 16; ++r) tmax = fmaxf(tmax, x[r]);
     const float mn = fmaxf(m, tmax);
     if (mn != -INFINITY) {
       float acc_l = 0.f;
 #pragma unroll
-      for (int r = 0; r < 16; ++r) acc_l += __builtin_amdgcn_exp2f(x[r] - mn);
+      for (int r = 0; r < 16; ++r) acc_l += __builtin_amdgcn_exp2f(pv[r] - mn);
       l = l * __builtin_amdgcn_exp2f(m - mn) + acc_l;
       m = mn;
     }
+    pjt = jt;
   }
+  store();
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // raw scores and the repeat load are done
   {
     const float mo = __shfl_xor(m, 32, 64), lo = __shfl_xor(l, 32, 64);
     const float mn = fmaxf(m, mo);
@@ -445,53 +279,40 @@ __global__ __launch_bounds__(512) void score_kernel_2p(const float *__restrict__
     row_m[l32] = M;
     row_inv[l32] = L > 0.f ? 1.f / L : 0.f;
   }
-  __syncthreads();
+  __syncthreads();  // also orders every wave's raw stores before the reads below
 
-  // ---- pass 2: recompute each tile, write P normalised; a tile's stores go
-  // out during the next tile
-  const float M = row_m[l32], inv = row_inv[l32];
-  float pv[16];
-  int pjt = -1;  // tile whose values pv holds
-  auto store = [&]() {
-    if (pjt < 0 || !row_ok) return;
+  // ---- pass 2: the group's rows in place, row-major: P = exp2(raw - M) / L
+  // on the causal tiles, zeros above them
+  const int jc = min(ntc * 32, nb);  // columns written in pass 1
+  if (vec) {
+    const int n4 = nb / 4, c4 = jc / 4;
+    constexpr int U = 8;  // loads in flight per thread
+    for (int e0 = threadIdx.x; e0 < rows * n4; e0 += U * NT) {
+      float4 v[U];
 #pragma unroll
-    for (int q4 = 0; q4 < 4; ++q4) {
-      const int J = pjt * 32 + q4 * 8 + half * 4;
-      if (vec && J + 3 < nb) {
-        *(float4 *)(prow + J) =
-            make_float4(pv[4 * q4], pv[4 * q4 + 1], pv[4 * q4 + 2], pv[4 * q4 + 3]);
-      } else {
+      for (int k = 0; k < U; ++k) {
+        const int e = e0 + k * NT, rr = e / n4, c = e - rr * n4;
+        v[k] = e < rows * n4 && c < c4 ? *(const float4 *)(pgrp + (size_t)rr * nb + 4 * c)
+                                       : make_float4(-INFINITY, -INFINITY, -INFINITY, -INFINITY);
+      }
 #pragma unroll
-        for (int e = 0; e < 4; ++e)
-          if (J + e < nb) prow[J + e] = pv[4 * q4 + e];
+      for (int k = 0; k < U; ++k) {
+        const int e = e0 + k * NT, rr = e / n4, c = e - rr * n4;
+        if (e < rows * n4) {
+          const float M = row_m[rr], inv = row_inv[rr];
+          *(float4 *)(pgrp + (size_t)rr * nb + 4 * c) =
+              make_float4(__builtin_amdgcn_exp2f(v[k].x - M) * inv,
+                          __builtin_amdgcn_exp2f(v[k].y - M) * inv,
+                          __builtin_amdgcn_exp2f(v[k].z - M) * inv,
+                          __builtin_amdgcn_exp2f(v[k].w - M) * inv);
+        }
       }
     }
-  };
-  for (int t = 0; t < nt; ++t) {
-    float x[16];
-    tile(t, 2 * nt + 2 * t, x, store);
-#pragma unroll
-    for (int r = 0; r < 16; ++r) pv[r] = __builtin_amdgcn_exp2f(x[r] - M) * inv;
-    pjt = w + NWV * t;
-  }
-  store();
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // the repeat load has landed before exit
-  // zeros above the causal tiles, all threads, row-major
-  float *pgrp = P + ((size_t)h * nb + I0) * nb;
-  const int jend = ntc * 32;
-  if (jend < nb) {
-    if (vec) {
-      const int n4 = (nb - jend) / 4;
-      for (int e = threadIdx.x; e < rows * n4; e += 512) {
-        const int rr = e / n4, J = jend + (e - rr * n4) * 4;
-        *(float4 *)(pgrp + (size_t)rr * nb + J) = make_float4(0.f, 0.f, 0.f, 0.f);
-      }
-    } else {
-      const int n1 = nb - jend;
-      for (int e = threadIdx.x; e < rows * n1; e += 512) {
-        const int rr = e / n1;
-        pgrp[(size_t)rr * nb + jend + (e - rr * n1)] = 0.f;
-      }
+  } else {
+    for (int e = threadIdx.x; e < rows * nb; e += NT) {
+      const int rr = e / nb, J = e - rr * nb;
+      float *p = pgrp + (size_t)rr * nb + J;
+      *p = J < jc ? __builtin_amdgcn_exp2f(*p - row_m[rr]) * row_inv[rr] : 0.f;
     }
   }
 }
@@ -500,13 +321,13 @@ template <int D, bool RESC>
 static hipError_t launch_score_t(const Shape &s, float c, const float *qp, const float *kp,
                                  const float *kr, float *S, hipStream_t st) {
   // heaviest row groups of every head first
-  dim3 grid(s.hq, (s.nb + 31) / 32);
-  if (s.nb <= 1024)
-    hipLaunchKernelGGL((score_kernel_reg<D, RESC>), grid, dim3(512), 0, st, qp, kp, kr, S, s.hq,
+  const dim3 grid(s.hq, (s.nb + 31) / 32);
+  if (s.nb % 4 == 0)
+    hipLaunchKernelGGL((score_kernel<D, RESC, true>), grid, dim3(256), 0, st, qp, kp, kr, S, s.hq,
                        s.hkv, s.nb, c * kLog2e);
   else
-    hipLaunchKernelGGL((score_kernel_2p<D, RESC>), grid, dim3(512), 0, st, qp, kp, kr, S, s.hq,
-                       s.hkv, s.nb, c * kLog2e);
+    hipLaunchKernelGGL((score_kernel<D, RESC, false>), grid, dim3(256), 0, st, qp, kp, kr, S,
+                       s.hq, s.hkv, s.nb, c * kLog2e);
   return hipGetLastError();
 }
 

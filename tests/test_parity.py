@@ -232,8 +232,8 @@ def _pooled_accuracy_case(which):
                                    "bf16_64_128_130", "bf16_64_64_1100", "fp8_128_128_1030"])
 @pytest.mark.parametrize("rescue", [False, True])
 def test_pooled_scores_at_fp32_accuracy(which, rescue):
-    """The pooled scores are as accurate as fp32 dot products (rows of up to
-    1024 blocks and longer ones, which take the other score kernel).
+    """The pooled scores are as accurate as fp32 dot products (rows of 45 to
+    1100 blocks, whole and ragged last tiles).
 
     Where P is at least 1e-6 of its row maximum, log P is within
     2e-6 + 2^-20 * c * sum_i |Qbar_i Kbar_i| of the fp64 oracle: the size of
@@ -268,7 +268,7 @@ def test_pooled_scores_at_fp32_accuracy(which, rescue):
 
 
 def test_long_rows_over_2048_blocks():
-    """nb = 2188: the general score kernel and the general mask path, base and
+    """nb = 2188: rows longer than 2048 blocks (the general mask path), base and
     rescue branches, against the oracle."""
     announce("long rows nb=2188")
     c = gen.make_case(2, 1, 2188 * 64, 64, 64, "bf16", 21, gamma=0.2, rope=True, n_vert=8,
