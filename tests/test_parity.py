@@ -295,6 +295,62 @@ def test_long_rows_over_2048_blocks():
                 omd, ocntd)
 
 
+
+@pytest.mark.parametrize("nb", [1022, 2047, 2190])
+def test_mask_long_rows_not_16_byte_aligned(nb):
+    """Rows of nb % 4 != 0 blocks, long enough that a row's kept list leaves
+    in several whole 256-entry runs while its rows are not 16-byte aligned:
+    the threshold path (register kernel up to 2048 blocks, the general one
+    beyond) against the oracle, and the caller-mask path against the causal
+    part of the mask itself."""
+    announce(f"long unaligned mask rows nb={nb}")
+    rng = np.random.default_rng(nb)
+    hq, block, gamma = 2, 64, 0.1
+    P = np.tril(rng.random((hq, nb, nb)) ** 2).astype(np.float32)
+    m, idx, cnt = bsp.mask(torch.from_numpy(P).cuda(), gamma, nb * block, block)
+    um = (rng.random((hq, nb, nb)) < 0.9).astype(np.uint8)
+    um[:, np.arange(nb), np.arange(nb)] = 1
+    m2, idx2, cnt2 = bsp.mask(None, gamma, nb * block, block, user_mask=torch.from_numpy(um).cuda())
+    torch.cuda.synchronize()
+    om, oidx, ocnt = oracle.mask(P.astype(np.float64), gamma)
+    H.check_mask(m.cpu().numpy(), idx.cpu().numpy(), cnt.cpu().numpy(),
+                 dict(P=P.astype(np.float64), mask=om, idx=oidx, cnt=ocnt), gamma)
+    assert int(cnt.max()) > 512  # rows with at least two whole runs
+    want = np.tril(um)
+    assert np.array_equal(m2.cpu().numpy(), want)
+    widx, wcnt = H.idx_from_mask(want)
+    gcnt = cnt2.cpu().numpy()
+    assert np.array_equal(gcnt, wcnt)
+    keep = np.arange(nb)[None, None, :] < wcnt[..., None]
+    assert np.array_equal(np.where(keep, idx2.cpu().numpy(), -1), widx)
+
+
+def test_mask_varlen_long_rows_unaligned_stride():
+    """Packed batch whose sequences have 301 and 270 blocks, idx_stride 302
+    (rows not 16-byte aligned): every row's kept list, from a caller mask,
+    against the mask itself."""
+    announce("varlen mask, long rows, idx_stride 302")
+    rng = np.random.default_rng(5)
+    hq, block = 2, 64
+    lens = [300 * block + 5, 270 * block]
+    nbs = [-(-n // block) for n in lens]
+    tb, stride = sum(nbs), max(nbs) + 1
+    um = (rng.random((hq, tb, stride)) < 0.9).astype(np.uint8)
+    m, idx, cnt = bsp.mask_varlen(None, 0.1, lens, block,
+                                  user_mask=torch.from_numpy(um).cuda())
+    torch.cuda.synchronize()
+    gm, gidx, gcnt = m.cpu().numpy(), idx.cpu().numpy(), cnt.cpu().numpy()
+    b0 = 0
+    for nb in nbs:
+        want = np.tril(um[:, b0:b0 + nb, :nb])
+        assert np.array_equal(gm[:, b0:b0 + nb, :nb], want)
+        widx, wcnt = H.idx_from_mask(want)
+        assert np.array_equal(gcnt[:, b0:b0 + nb], wcnt)
+        keep = np.arange(nb)[None, None, :] < wcnt[..., None]
+        assert np.array_equal(np.where(keep, gidx[:, b0:b0 + nb, :nb], -1), widx)
+        b0 += nb
+    assert int(gcnt.max()) > 256
+
 _NAN_BITS = {"bf16": 0x7FC0, "fp8": 0x7F}
 
 
