@@ -272,8 +272,9 @@ def score_rescue(k: torch.Tensor, q_pool: torch.Tensor, k_pool: torch.Tensor, se
 
 
 def mask_dual(score_t: torch.Tensor, rescue_t: torch.Tensor, gamma: float, gamma_rescue: float,
-              seq: int, block: int, sink_blocks: int = 1, local_blocks: int = 1):
-    """Both branches thresholded and combined.  Returns (mask, kv_idx, kv_cnt)."""
+              seq: int, block: int, sink_blocks: int = 1, local_blocks: int = 1,
+              want_mask: bool = True):
+    """Both branches thresholded and combined.  Returns (mask or None, kv_idx, kv_cnt)."""
     hq, nb, _ = score_t.shape
     if nb != -(-seq // block):
         raise BspError(2, "score does not match seq and block")
@@ -283,7 +284,8 @@ def mask_dual(score_t: torch.Tensor, rescue_t: torch.Tensor, gamma: float, gamma
             raise BspError(3, f"{name} must be float32")
     dsc = desc(hq, 1, seq, 64, block, DTYPE_F32, gamma=gamma, sink_blocks=sink_blocks,
                local_blocks=local_blocks)
-    m = torch.empty((hq, nb, nb), dtype=torch.uint8, device=score_t.device)
+    m = (torch.empty((hq, nb, nb), dtype=torch.uint8, device=score_t.device) if want_mask
+         else None)
     idx = torch.empty((hq, nb, nb), dtype=torch.int32, device=score_t.device)
     cnt = torch.empty((hq, nb), dtype=torch.int32, device=score_t.device)
     _check(bsp_mask_dual(dsc, _ptr(score_t), _ptr(rescue_t), gamma_rescue, _ptr(m), _ptr(idx),
@@ -315,9 +317,10 @@ def mask(score_t: Optional[torch.Tensor], gamma: float, seq: int, block: int,
 
 
 def calibrate_gamma(score_t: torch.Tensor, seq: int, block: int, target: float,
-                    tol: float = 1e-4, sink_blocks: int = 1, local_blocks: int = 1):
+                    tol: float = 1e-4, sink_blocks: int = 1, local_blocks: int = 1,
+                    want_mask: bool = True):
     """Threshold factor for a target density (bsp_calibrate_gamma; blocks the
-    host).  Returns (gamma, density, mask, kv_idx, kv_cnt) at that gamma."""
+    host).  Returns (gamma, density, mask or None, kv_idx, kv_cnt) at that gamma."""
     hq, nb, _ = score_t.shape
     if nb != -(-seq // block):
         raise BspError(2, "score does not match seq and block")
@@ -326,7 +329,8 @@ def calibrate_gamma(score_t: torch.Tensor, seq: int, block: int, target: float,
         raise BspError(3, "score must be float32")
     dsc = desc(hq, 1, seq, 64, block, DTYPE_F32, sink_blocks=sink_blocks,
                local_blocks=local_blocks)
-    m = torch.empty((hq, nb, nb), dtype=torch.uint8, device=score_t.device)
+    m = (torch.empty((hq, nb, nb), dtype=torch.uint8, device=score_t.device) if want_mask
+         else None)
     idx = torch.empty((hq, nb, nb), dtype=torch.int32, device=score_t.device)
     cnt = torch.empty((hq, nb), dtype=torch.int32, device=score_t.device)
     host = torch.empty((hq * nb,), dtype=torch.int32)

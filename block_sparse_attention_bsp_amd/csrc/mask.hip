@@ -64,6 +64,8 @@ struct KeptList {
     }
     n += total;
     if (n - flushed >= 256) {  // at most 511 wait, so one run per step
+      // lanes read entries other lanes stored: order the LDS accesses
+      wave_lds_sync();
       const int4 v = *(const int4 *)&ring[(flushed & 511) + 4 * lane];
       int32_t *d = dst + flushed + 4 * lane;
       if (vec) {
@@ -72,10 +74,12 @@ struct KeptList {
         d[0] = v.x; d[1] = v.y; d[2] = v.z; d[3] = v.w;
       }
       flushed += 256;
+      wave_lds_sync();  // the next push may overwrite the slots just read
     }
   }
   // the last n - flushed (< 256) entries; returns the row's count
   __device__ __forceinline__ int finish() {
+    wave_lds_sync();
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       const int i = flushed + 4 * lane + e;
@@ -249,13 +253,15 @@ __global__ __launch_bounds__(256) void mask_kernel_reg(const float *__restrict__
       keep[e] = Je <= I && (x[t][e] >= thr || (DUAL && y[DUAL ? t : 0][e] >= thr_r) ||
                             Je < sink || I - Je < local);
     }
-    if (vec && J + 3 < nb) {
-      *(uint32_t *)(mask + off + J) = (uint32_t)keep[0] | ((uint32_t)keep[1] << 8) |
-                                      ((uint32_t)keep[2] << 16) | ((uint32_t)keep[3] << 24);
-    } else {
+    if (mask) {  // the block mask is optional (wave-uniform branch)
+      if (vec && J + 3 < nb) {
+        *(uint32_t *)(mask + off + J) = (uint32_t)keep[0] | ((uint32_t)keep[1] << 8) |
+                                        ((uint32_t)keep[2] << 16) | ((uint32_t)keep[3] << 24);
+      } else {
 #pragma unroll
-      for (int e = 0; e < 4; ++e)
-        if (J + e < nb) mask[off + J + e] = keep[e] ? 1 : 0;
+        for (int e = 0; e < 4; ++e)
+          if (J + e < nb) mask[off + J + e] = keep[e] ? 1 : 0;
+      }
     }
     kl.push(keep, J);
   }
