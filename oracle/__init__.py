@@ -179,32 +179,42 @@ def mask(P: Optional[np.ndarray], gamma: float, sink_blocks: int = 1, local_bloc
     return m, idx, cnt
 
 
-def calibrate_gamma(P: np.ndarray, target: float, tol: float = 1e-4, sink_blocks: int = 1,
-                    local_blocks: int = 1):
+def calibrate_gamma(P: np.ndarray, target: float, sink_blocks: int = 1, local_blocks: int = 1):
     """The threshold factor that keeps a target share of the causal blocks
     (FlashPrefill summary page, Appendix A "Hyperparameter Configurations":
-    the threshold is calibrated on computational density).  density(gamma) is
-    the kept share of causal blocks under ``mask``; it never increases with
-    gamma, so bisection on [0, 1] with float32 midpoints returns the largest
-    gamma (to within tol) whose density is at least target, or 1 when gamma = 1
-    already keeps it.  Returns (gamma, density)."""
+    the single threshold hyperparameter is calibrated on computational
+    density, with block size and structural retention fixed).
+
+    Definition: density(gamma) = kept causal blocks / causal blocks under the
+    mask rule (P >= gamma * row max, or forced), and the answer is the
+    largest gamma in [0, 1] with density(gamma) >= target.  Written out: a
+    causal block that is not forced is kept exactly when its ratio
+    r = P / row max is at least gamma, so kept(gamma) = forced + #{r >= gamma}.
+    If gamma = 1 already keeps the target, the answer is 1.  Otherwise it is
+    the n-th largest ratio, n = (fewest kept blocks that reach the target) -
+    forced: at that ratio n blocks are kept, and above it fewer than n.
+    Returns (gamma, density) in float64."""
+    P = np.asarray(P, np.float64)
     hq, nb, _ = P.shape
-    causal = hq * nb * (nb + 1) / 2.0
-
-    def density(g):
-        return mask(P, float(g), sink_blocks, local_blocks)[2].sum() / causal
-
-    d = density(np.float32(1.0))
-    if d >= target:
-        return 1.0, float(d)
-    lo, hi = np.float32(0.0), np.float32(1.0)
-    while hi - lo > np.float32(tol):
-        mid = np.float32(0.5) * (lo + hi)
-        if density(mid) >= target:
-            lo = mid
-        else:
-            hi = mid
-    return float(lo), float(density(lo))
+    I = np.arange(nb)[:, None]
+    J = np.arange(nb)[None, :]
+    causal = np.broadcast_to(J <= I, P.shape)
+    forced = causal & np.broadcast_to((J < sink_blocks) | (I - J < local_blocks), P.shape)
+    total = hq * nb * (nb + 1) // 2
+    pmax = np.where(causal, P, -np.inf).max(-1, keepdims=True)
+    ratio = P / pmax
+    free = causal & ~forced
+    n_forced = int(forced.sum())
+    # fewest kept blocks k with k / total >= target, as the density compares
+    k = max(0, int(math.ceil(target * total)) - 1)
+    while k / total < target:
+        k += 1
+    at_one = n_forced + int((free & (ratio >= 1.0)).sum())
+    if at_one >= k:
+        return 1.0, at_one / total
+    r = np.sort(ratio[free])[::-1]
+    g = float(r[k - n_forced - 1])
+    return g, (n_forced + int((r >= g).sum())) / total
 
 
 def attn(q, k, v, dtype: str, block: int, block_mask: np.ndarray, sm_scale: Optional[float] = None,

@@ -341,11 +341,11 @@ def test_mask_dual_union_and_zero_radius_reduction():
         assert np.array_equal(oracle.mask_dual(P, P0, g, gr)[0], oracle.mask(P, min(g, gr))[0])
 
 
-def _exact_calibration(P, target, sink, local):
+def _exhaustive_calibration(P, target, sink, local):
     """Exhaustive answer: density only changes at the ratios P / row max, so
-    the largest gamma with density >= target is the largest such ratio (or 1)
-    whose kept share reaches the target.  Evaluated by counting, not through
-    the oracle's mask."""
+    try every candidate (each distinct ratio of a causal block, and 1),
+    count the kept blocks at it, and keep the largest candidate whose kept
+    share reaches the target.  No sorting or order statistic."""
     hq, nb, _ = P.shape
     I = np.arange(nb)[:, None]
     J = np.arange(nb)[None, :]
@@ -356,7 +356,7 @@ def _exact_calibration(P, target, sink, local):
     total = hq * nb * (nb + 1) / 2
 
     def dens(g):
-        return ((causal & (P >= g * pmax)) | forced).sum() / total
+        return ((causal & (ratios >= g)) | forced).sum() / total
 
     if dens(1.0) >= target:
         return 1.0
@@ -367,21 +367,23 @@ def _exact_calibration(P, target, sink, local):
     return best
 
 
-@pytest.mark.parametrize("seed,target", [(0, 0.3), (1, 0.5), (2, 0.7), (3, 0.9), (0, 0.05)])
-def test_calibrate_gamma_brackets_the_exact_answer(seed, target):
+@pytest.mark.parametrize("seed,target,sink,local", [(0, 0.3, 1, 1), (1, 0.5, 1, 1),
+                                                     (2, 0.7, 1, 1), (3, 0.9, 1, 1),
+                                                     (0, 0.05, 1, 1), (1, 0.6, 2, 4),
+                                                     (2, 0.4, 4, 8), (3, 0.8, 0, 0)])
+def test_calibrate_gamma_is_the_exact_answer(seed, target, sink, local):
     c = gen.make_s1(seed)
     _, P, _ = _pipeline(c, 0.1)
-    tol = 1e-4
-    g, d = oracle.calibrate_gamma(P, target, tol)
-    exact = _exact_calibration(P, target, 1, 1)
-    assert d >= target
-    if exact == 1.0:
-        assert g == 1.0
-    else:
-        assert exact - tol <= g <= exact
-        # just above the exact answer the density falls below the target
-        _, _, cnt = oracle.mask(P, min(1.0, exact + 1e-7), 1, 1)
-        assert cnt.sum() / (c.hq * c.nb * (c.nb + 1) / 2) < target
+    g, d = oracle.calibrate_gamma(P, target, sink, local)
+    exact = _exhaustive_calibration(P, target, sink, local)
+    assert g == exact
+    total = c.hq * c.nb * (c.nb + 1) / 2
+    # the oracle's own mask reaches the target at gamma and misses it just above
+    _, _, cnt = oracle.mask(P, g * (1 - 1e-12), sink, local)
+    assert cnt.sum() / total >= target and abs(cnt.sum() / total - d) < 1e-12
+    if g < 1.0:
+        _, _, cnt = oracle.mask(P, g * (1 + 1e-9), sink, local)
+        assert cnt.sum() / total < target
 
 
 def test_calibrate_gamma_edges_and_monotone_in_target():
