@@ -69,6 +69,11 @@ def parse():
                         "1K-32K tokens, 128K in all) over a shuffled paged cache")
     p.add_argument("--calibrate", type=float, default=None, metavar="TARGET",
                    help="also time bsp_calibrate_gamma for this target density")
+    p.add_argument("--sink", type=int, default=1,
+                   help="sink blocks always kept (the pages keep 256 tokens: 2 at block 128)")
+    p.add_argument("--local", type=int, default=1,
+                   help="local-window blocks always kept, the diagonal included (the pages "
+                        "keep 512 tokens: 4 at block 128)")
     p.add_argument("--copy-calibration", action="store_true",
                    help="also run one 1 GiB device copy (HBM counter calibration)")
     return p.parse_args()
@@ -78,13 +83,27 @@ def dense_flops(hq, seq, d):
     return 4.0 * d * hq * seq * (seq + 1) / 2.0
 
 
-def kept_flops(cnt: np.ndarray, d: int, block: int, seq: int) -> float:
+def kept_flops(cnt: np.ndarray, d: int, block: int, seq: int, n_diag=None) -> float:
     """4*d*sum over kept (h, I, J) of the causal pairs in the tile (B^2 off
-    the diagonal, B(B+1)/2 on it; ragged tails are not in the configs)."""
+    the diagonal, B(B+1)/2 on it; ragged tails are not in the configs).
+    n_diag: kept diagonal tiles (default: every row keeps its diagonal, as
+    with a local window of at least one block)."""
     nb = cnt.shape[1]
     tot = cnt.astype(np.float64).sum()
-    diag = cnt.shape[0] * nb  # the diagonal is always kept (local window of 1)
+    diag = cnt.shape[0] * nb if n_diag is None else float(n_diag)
     return 4.0 * d * ((tot - diag) * block * block + diag * block * (block + 1) / 2.0)
+
+
+def cpu_model() -> str:
+    """The host CPU's model name (Linux /proc/cpuinfo), or 'unknown'."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for ln in f:
+                if ln.startswith("model name"):
+                    return ln.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
 
 
 def scoring_bytes(hq, hkv, seq, d, block, es, kept_entries):
@@ -119,30 +138,45 @@ def traffic_from_note():
     return float(m_b.group(1)) if cur == m_sha.group(1) else None
 
 
-def cpu_baseline(case, gpu_mask, nrows):
-    """Oracle (as it stands) on the host: stages 1-2 on the whole layer, stage
-    3 on a uniform sample of query rows; extrapolated to the layer by FLOPs."""
+def cpu_baseline(case, nrows, sink=1, local=1, user_mask=None):
+    """Oracle (as it stands) on the host: pool, score and mask on the whole
+    layer, each timed, then attention on a uniform sample of query rows;
+    the layer time extrapolates the attention by dense-causal FLOPs."""
     import oracle
+    c = 1.0 / math.sqrt(case.d)
+    t = {}
     t0 = time.perf_counter()
-    orc = oracle.prefill(case, with_attn=False)
-    t12 = time.perf_counter() - t0
+    qbar = oracle.pool(case.q, case.dtype, case.block, case.q_scale)
+    kbar = oracle.pool(case.k, case.dtype, case.block, case.k_scale)
+    t["pool"] = time.perf_counter() - t0
+    P = None
+    if user_mask is None:
+        t0 = time.perf_counter()
+        _, P = oracle.score(qbar, kbar, c)
+        t["score"] = time.perf_counter() - t0
+    t0 = time.perf_counter()
+    m, _, _ = oracle.mask(P, case.gamma, sink, local, user_mask=user_mask)
+    t["mask"] = time.perf_counter() - t0
     per_head = max(1, nrows // case.hq)
     pos = np.unique(np.linspace(0, case.seq - 1, per_head).astype(np.int64))
     rows = (np.arange(case.hq)[:, None] * case.seq + pos[None, :]).reshape(-1)
     t0 = time.perf_counter()
-    oracle.attn(case.q, case.k, case.v, case.dtype, case.block, orc["mask"],
+    oracle.attn(case.q, case.k, case.v, case.dtype, case.block, m,
                 q_scale=case.q_scale, k_scale=case.k_scale, v_scale=case.v_scale, rows=rows)
-    t3 = time.perf_counter() - t0
+    t_rows = time.perf_counter() - t0
     # dense-causal work of the sampled rows: query i sees i+1 keys
     samp = 4.0 * case.d * float((pos + 1).sum()) * case.hq
     full = dense_flops(case.hq, case.seq, case.d)
-    t_layer = t12 + t3 * full / samp
+    t["attn"] = t_rows * full / samp
+    t_layer = sum(t.values())
     return {
         "value": round(full / t_layer / 1e12, 6), "unit": "TFLOP/s", "cores": oracle.threads(),
-        "kind": "oracle",
-        "sample": (f"pool+score+mask on the whole layer ({t12:.2f}s) + attention for "
-                   f"{rows.size} query rows ({per_head} uniformly spaced per head, {t3:.2f}s), "
-                   f"extrapolated by dense-causal FLOPs to one layer = {t_layer:.1f}s"),
+        "kind": "oracle", "cpu_model": cpu_model(),
+        "stage_s": {k: round(v, 3) for k, v in t.items()},
+        "sample": (f"pool, score and mask on the whole layer ({t['pool'] + t.get('score', 0.0) + t['mask']:.2f}s) + "
+                   f"attention for {rows.size} query rows ({per_head} uniformly spaced per head, "
+                   f"{t_rows:.2f}s; oracle mask), attention extrapolated by dense-causal FLOPs "
+                   f"to the layer = {t['attn']:.1f}s; layer {t_layer:.1f}s"),
     }
 
 
@@ -288,7 +322,7 @@ def main():
     o = torch.empty((hq, seq, d), dtype=f32 if c.dtype == "f32" else torch.bfloat16, device=dev)
     lse = torch.empty((hq, seq), dtype=f32, device=dev)
     dsc = bsp.desc(hq, hkv, seq, d, B, {"f32": 0, "bf16": 1, "fp8": 2}[c.dtype], gamma=c.gamma,
-                   q_scale=qs, k_scale=ks, v_scale=vs)
+                   sink_blocks=a.sink, local_blocks=a.local, q_scale=qs, k_scale=ks, v_scale=vs)
     P = bsp._ptr
     stream = torch.cuda.current_stream()
     sp = bsp._stream()
@@ -326,15 +360,19 @@ def main():
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     ms_step = wall * 1e3 / a.steps
-    st_score = float(np.mean([e[0].elapsed_time(e[1]) for e in evs]))
-    st_mask = float(np.mean([e[1].elapsed_time(e[2]) for e in evs]))
-    st_attn = float(np.mean([e[2].elapsed_time(e[3]) for e in evs]))
+    # per-stage times: the median over the timed steps (HIP events on the
+    # stream the kernels run on)
+    st_score = float(np.median([e[0].elapsed_time(e[1]) for e in evs]))
+    st_mask = float(np.median([e[1].elapsed_time(e[2]) for e in evs]))
+    st_attn = float(np.median([e[2].elapsed_time(e[3]) for e in evs]))
+    st_attn_mean = float(np.mean([e[2].elapsed_time(e[3]) for e in evs]))
 
     cnt_h = cnt.cpu().numpy()
     kept_entries = int(cnt_h.sum())
     density = kept_entries / (hq * nb * (nb + 1) / 2)
     F_dense = dense_flops(hq, seq, d)
-    F_kept = kept_flops(cnt_h, d, B, seq)
+    n_diag = int(np.diagonal(mk.cpu().numpy(), axis1=1, axis2=2).astype(bool).sum())
+    F_kept = kept_flops(cnt_h, d, B, seq, n_diag)
     peak = PEAK_FP8_TFLOPS if c.dtype == "fp8" else PEAK_BF16_TFLOPS
     achieved = F_kept / (st_attn * 1e-3) / 1e12
     es = {"f32": 4, "bf16": 2, "fp8": 1}[c.dtype]
@@ -364,18 +402,20 @@ def main():
     if a.calibrate is not None and um is None:
         torch.cuda.synchronize()
         t0 = time.perf_counter()
-        g, dens, _, _, _ = bsp.calibrate_gamma(sc, seq, B, a.calibrate)
+        g, dens, _, _, _ = bsp.calibrate_gamma(sc, seq, B, a.calibrate, sink_blocks=a.sink,
+                                               local_blocks=a.local)
         torch.cuda.synchronize()
         calib = {"target": a.calibrate, "gamma": round(g, 6), "density": round(dens, 6),
                  "ms": round((time.perf_counter() - t0) * 1e3, 3)}
 
     cpu = None
     if not a.no_cpu:
-        cpu = cpu_baseline(c, mk.cpu().numpy(), a.cpu_rows)
+        cpu = cpu_baseline(c, a.cpu_rows, a.sink, a.local,
+                           None if um is None else um.cpu().numpy())
 
     traffic = traffic_from_note() if (a.config == 3 and a.seq is None and um is None
                                       and not a.s2 and a.scorer == "pooled"
-                                      and not resc) else None
+                                      and not resc and a.sink == 1 and a.local == 1) else None
     wl = (f"{c.name}: {hq} q / {hkv} kv heads, seq {seq}, d {d}, block {B}, gamma {c.gamma}, "
           f"causal, {c.dtype}, batch 1, one layer")
     if um is not None:
@@ -386,6 +426,8 @@ def main():
         wl += ", per-query block-approximation scorer"
     if resc:
         wl += f", rescue branch gamma_r {a.rescue}"
+    if a.sink != 1 or a.local != 1:
+        wl += f", sink {a.sink} / local {a.local} blocks"
     out = {
         "metric": "sparse prefill-attn ms/layer + effective TFLOP/s at 128K bf16; % MFMA peak",
         "value": round(F_dense / (ms_step * 1e-3) / 1e12, 3),
@@ -398,7 +440,8 @@ def main():
                    "block": B, "gamma": c.gamma, "batch": 1, "parallelism": "none (1 GPU)"},
         "ms_per_layer": round(ms_step, 4),
         "stage_ms": {"score": round(st_score, 4), "mask": round(st_mask, 4),
-                     "attn": round(st_attn, 4)},
+                     "attn": round(st_attn, 4), "stat": f"median of {a.steps} steps",
+                     "attn_mean": round(st_attn_mean, 4)},
         "density": round(density, 6),
         "kept_tflops": round(achieved, 3),
         "mfma_peak_frac": round(achieved / peak, 4),

@@ -77,14 +77,24 @@ def test_scoring_bytes_at_128k_equal_the_three_kernels_algorithmic_bytes(bench):
 
 
 def test_traffic_is_reported_only_for_the_counted_sources(bench, tmp_path, monkeypatch):
-    """The committed note's traffic figure is returned while the attention
-    sources hash to the fingerprint it records, and dropped once they do not."""
-    t = bench.traffic_from_note()
-    assert t is not None and 2.7e9 < t < 1e11
+    """A counter note's traffic figure is returned while the attention
+    sources hash to the fingerprint it records, and dropped once they do not
+    (a note written here, so the check does not depend on which sources the
+    committed note was taken on)."""
+    import hashlib
+    h = hashlib.sha256()
+    for f in bench.ATTN_SRCS:
+        h.update(open(f, "rb").read())
+    note = tmp_path / "note.md"
+    note.write_text(f"source_sha256: {h.hexdigest()}\ntraffic_bytes_per_launch: 2.1e10\n")
+    monkeypatch.setattr(bench, "PMC_NOTE", str(note))
+    assert bench.traffic_from_note() == 2.1e10
     changed = []
     for f in bench.ATTN_SRCS:
         p = tmp_path / os.path.basename(f)
         p.write_bytes(open(f, "rb").read() + b"\n// edited\n")
         changed.append(str(p))
     monkeypatch.setattr(bench, "ATTN_SRCS", changed)
+    assert bench.traffic_from_note() is None
+    monkeypatch.setattr(bench, "PMC_NOTE", str(tmp_path / "missing.md"))
     assert bench.traffic_from_note() is None

@@ -177,9 +177,9 @@ def test_score_arith_matches_oracle(which):
     print(f"  density {dens:.3f} band blocks {nband}", flush=True)
 
 
-def _check_dual(gm, gidx, gcnt, P, Pr, g, gr, om, ocnt):
+def _check_dual(gm, gidx, gcnt, P, Pr, g, gr, om, ocnt, sink=1, local=1):
     """Dual mask equal to the oracle's outside either branch's band."""
-    b = H.band(P, g, 1, 1) | H.band(Pr, gr, 1, 1)
+    b = H.band(P, g, sink, local) | H.band(Pr, gr, sink, local)
     diff = gm != om
     assert not np.any(diff & ~b), f"{int((diff & ~b).sum())} blocks differ outside the bands"
     want_idx, want_cnt = H.idx_from_mask(gm)
@@ -421,15 +421,60 @@ def test_varlen_paged_matches_oracle_per_sequence(dtype, d, block, dense):
     print(f"  max-abs O err {err:.2e}", flush=True)
 
 
-@pytest.mark.parametrize("dtype,d,block,gamma", [("bf16", 128, 128, 0.3), ("fp8", 128, 128, 0.2),
-                                                  ("bf16", 64, 64, 0.4), ("fp8", 64, 64, 0.3)])
-def test_varlen_pipeline_matches_oracle_per_sequence(dtype, d, block, gamma):
+@pytest.mark.parametrize("dtype", ["bf16", "fp8"])
+def test_varlen_block_order(dtype):
+    """A caller's launch order (block_order, a permutation of the batch's
+    query blocks) changes only which workgroup serves a row: the output is
+    bit-identical to the default order and matches the oracle per sequence."""
+    lens = [1000, 130, 512, 64, 777, 1, 1200]
+    d, block = 128, 128
+    announce(f"varlen block_order {dtype} lens={lens}")
+    c, kc, vc, ptab, masks, nbs = _varlen_case(dtype, d, block, lens, 91, 0.5)
+    dv = H.dev(c)
+    t = lambda x: (torch.from_numpy(x.view(np.int16)).cuda().view(torch.bfloat16) if dtype == "bf16"
+                   else torch.from_numpy(x).cuda())
+    stride = max(nbs)
+    tb = sum(nbs)
+    idx = np.zeros((c.hq, tb, stride), np.int32)
+    cnt = np.zeros((c.hq, tb), np.int32)
+    b0 = 0
+    for m, nb in zip(masks, nbs):
+        i_s, c_s = H.idx_from_mask(m)
+        idx[:, b0:b0 + nb, :nb] = i_s
+        cnt[:, b0:b0 + nb] = c_s
+        b0 += nb
+    order = np.random.default_rng(5).permutation(tb).astype(np.int32)
+    kw = dict(q_scale=dv["q_scale"], k_scale=dv["k_scale"], v_scale=dv["v_scale"])
+    args = (dv["q"], t(kc), t(vc), torch.from_numpy(ptab).cuda(), lens, block,
+            torch.from_numpy(idx).cuda(), torch.from_numpy(cnt).cuda())
+    o1, l1 = bsp.attn_fwd_varlen(*args, **kw)
+    o2, l2 = bsp.attn_fwd_varlen(*args, block_order=torch.from_numpy(order).cuda(), **kw)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+    go, gl = o2.float().cpu().numpy(), l2.cpu().numpy()
+    t0, err = 0, 0.0
+    for n, nb, m in zip(lens, nbs, masks):
+        sl = slice(t0, t0 + n)
+        oo, ol = oracle.attn(c.q[:, sl], c.k[:, sl], c.v[:, sl], dtype, block, m,
+                             q_scale=c.q_scale, k_scale=c.k_scale, v_scale=c.v_scale)
+        err = max(err, H.check_attn(go[:, sl].reshape(-1, d), gl[:, sl].reshape(-1),
+                                    oo.reshape(-1, d), ol.reshape(-1), dtype))
+        t0 += n
+    print(f"  max-abs O err {err:.2e}", flush=True)
+
+
+@pytest.mark.parametrize("dtype,d,block,gamma,sink,local", [
+    ("bf16", 128, 128, 0.3, 1, 1), ("fp8", 128, 128, 0.2, 1, 1), ("bf16", 64, 64, 0.4, 1, 1),
+    ("fp8", 64, 64, 0.3, 1, 1), ("bf16", 128, 128, 0.3, 2, 4), ("fp8", 64, 64, 0.4, 4, 8)])
+def test_varlen_pipeline_matches_oracle_per_sequence(dtype, d, block, gamma, sink, local):
     """Score, mask and attention of a packed batch over a shuffled paged cache
     (unused cache rows NaN bits): every sequence against the oracle run on
-    that sequence alone."""
+    that sequence alone.  Includes the pages' sink and window sizes, counted
+    from each sequence's own first block."""
     import dataclasses
     lens = [1000, 130, 512, 64, 777, 1, 900]
-    announce(f"varlen pipeline {dtype} d={d} B={block} gamma={gamma} lens={lens}")
+    announce(f"varlen pipeline {dtype} d={d} B={block} gamma={gamma} sink={sink} local={local} "
+             f"lens={lens}")
     c = gen.make_case(4, 2, sum(lens), d, block, dtype, 47 + d, rope=True, n_vert=4,
                       block_offset=1.5)  # masks keep 45-73% of the causal blocks
     rng = np.random.default_rng(d + block)
@@ -454,8 +499,8 @@ def test_varlen_pipeline_matches_oracle_per_sequence(dtype, d, block, gamma):
     t = lambda x: (torch.from_numpy(x.view(np.int16)).cuda().view(torch.bfloat16) if dtype == "bf16"
                    else torch.from_numpy(x).cuda())
     res = bsp.prefill_varlen(dv["q"], t(kc), t(vc), torch.from_numpy(ptab).cuda(), lens, block,
-                             gamma, q_scale=dv["q_scale"], k_scale=dv["k_scale"],
-                             v_scale=dv["v_scale"])
+                             gamma, sink_blocks=sink, local_blocks=local, q_scale=dv["q_scale"],
+                             k_scale=dv["k_scale"], v_scale=dv["v_scale"])
     torch.cuda.synchronize()
     g = {k_: v_.cpu().numpy() for k_, v_ in res.items() if v_ is not None and k_ not in ("o", "lse")}
     go, gl = res["o"].float().cpu().numpy(), res["lse"].cpu().numpy()
@@ -463,13 +508,14 @@ def test_varlen_pipeline_matches_oracle_per_sequence(dtype, d, block, gamma):
     for n, nb in zip(lens, nbs):
         sub = dataclasses.replace(c, seq=n, q=c.q[:, t0:t0 + n], k=c.k[:, t0:t0 + n],
                                   v=c.v[:, t0:t0 + n])
-        orc = oracle.prefill(sub, gamma, with_attn=False)
+        orc = oracle.prefill(sub, gamma, sink_blocks=sink, local_blocks=local, with_attn=False)
         rb = slice(cb, cb + nb)
         np.testing.assert_allclose(g["q_pool"][:, rb], orc["qbar"], rtol=1e-5, atol=2e-6)
         np.testing.assert_allclose(g["k_pool"][:, rb], orc["kbar"], rtol=1e-5, atol=2e-6)
         np.testing.assert_allclose(g["score"][:, rb, :nb], orc["P"], rtol=1e-4, atol=1e-6)
         gm = g["mask"][:, rb, :nb]
-        nband += H.check_mask(gm, g["kv_idx"][:, rb, :nb], g["kv_cnt"][:, rb], orc, gamma)
+        nband += H.check_mask(gm, g["kv_idx"][:, rb, :nb], g["kv_cnt"][:, rb], orc, gamma, sink,
+                              local)
         oo, ol = oracle.attn(sub.q, sub.k, sub.v, dtype, block, gm, q_scale=c.q_scale,
                              k_scale=c.k_scale, v_scale=c.v_scale)
         sl = slice(t0, t0 + n)
@@ -481,26 +527,104 @@ def test_varlen_pipeline_matches_oracle_per_sequence(dtype, d, block, gamma):
     print(f"  density {dens:.3f} band {nband} max-abs O err {err:.2e}", flush=True)
 
 
-@pytest.mark.parametrize("which,target", [("s1_0", 0.3), ("s1_1", 0.7), ("llama_4k", 0.7)])
-def test_calibrate_gamma_matches_oracle(which, target):
-    """Bisection on the GPU masks lands on the oracle's gamma; the buffers
-    it leaves behind are the mask at that gamma."""
-    announce(f"calibrate gamma {which} target {target}")
+@pytest.mark.parametrize("which,target,sink,local", [
+    ("s1_0", 0.3, 1, 1), ("s1_1", 0.7, 1, 1), ("llama_4k", 0.7, 1, 1), ("s1_2", 0.5, 4, 8),
+    ("llama_4k", 0.7, 2, 4), ("s1_3", 0.9, 0, 0)])
+def test_calibrate_gamma_meets_the_definition(which, target, sink, local):
+    """bsp_calibrate_gamma against the definition (the largest gamma whose
+    density reaches the target, computed exactly by the oracle): the GPU's
+    gamma lies at most tol below it, up to the threshold band; its density
+    reaches the target and is the density of its own returned counts, which
+    match the oracle's mask at that gamma outside the band; the buffers it
+    leaves are bsp_mask's result at that gamma.  Includes the pages' sink
+    and window sizes."""
+    announce(f"calibrate gamma {which} target {target} sink {sink} local {local}")
     c = gen.make_s1(int(which[-1])) if which.startswith("s1") else gen.make_config(1)
     d = H.dev(c)
     _, _, sc = bsp.score(d["q"], d["k"], c.block, q_scale=d["q_scale"], k_scale=d["k_scale"])
     tol = 1e-4
-    g, dens, m, idx, cnt = bsp.calibrate_gamma(sc, c.seq, c.block, target, tol)
+    g, dens, m, idx, cnt = bsp.calibrate_gamma(sc, c.seq, c.block, target, tol, sink, local)
+    _, _, idx0, cnt0 = bsp.calibrate_gamma(sc, c.seq, c.block, target, tol, sink, local,
+                                           want_mask=False)[1:]
     torch.cuda.synchronize()
     orc = oracle.prefill(c, with_attn=False)
-    og, odens = oracle.calibrate_gamma(orc["P"], float(np.float32(target)), tol)
-    print(f"  gpu gamma {g:.6f} density {dens:.4f}; oracle gamma {og:.6f} density {odens:.4f}",
+    t32 = float(np.float32(target))
+    exact, edens = oracle.calibrate_gamma(orc["P"], t32, sink, local)
+    total = c.hq * c.nb * (c.nb + 1) / 2
+    gcnt = cnt.cpu().numpy()
+    print(f"  gpu gamma {g:.6f} density {dens:.4f}; exact gamma {exact:.6f} density {edens:.4f}",
           flush=True)
     assert dens >= np.float32(target)
-    assert abs(g - og) <= tol and abs(dens - odens) <= 2.0 / (c.hq * c.nb * (c.nb + 1) / 2)
-    m2, idx2, cnt2 = bsp.mask(sc, g, c.seq, c.block)
+    assert abs(dens - gcnt.sum() / total) <= 1e-6
+    band = H.MASK_BAND
+    if exact == 1.0:
+        assert g == 1.0
+    else:
+        assert exact * (1 - band) - tol <= g <= exact * (1 + band)
+    om, oidx, ocnt = oracle.mask(orc["P"], float(g), sink, local)
+    nb_ = H.check_mask(m.cpu().numpy(), idx.cpu().numpy(), gcnt,
+                       dict(P=orc["P"], mask=om, idx=oidx, cnt=ocnt), float(g), sink, local)
+    assert abs(gcnt.sum() - ocnt.sum()) <= nb_
+    m2, idx2, cnt2 = bsp.mask(sc, g, c.seq, c.block, sink, local)
     torch.cuda.synchronize()
-    assert torch.equal(m, m2) and torch.equal(cnt, cnt2)
+    assert torch.equal(m, m2) and torch.equal(cnt, cnt2) and torch.equal(cnt0, cnt2)
+    keep = torch.arange(c.nb, device=cnt.device)[None, None, :] < cnt2[..., None]
+    assert torch.equal(idx[keep], idx2[keep]) and torch.equal(idx0[keep], idx2[keep])
+
+
+@pytest.mark.parametrize("nb,block,sink,local", [(40, 128, 2, 4), (300, 64, 4, 8),
+                                                 (1022, 128, 2, 4), (2047, 64, 4, 8),
+                                                 (2190, 64, 4, 8), (2190, 128, 2, 4)])
+def test_mask_page_retention(nb, block, sink, local):
+    """The pages' structural retention (a 256-token sink and a 512-token
+    window: 2 and 4 blocks at B = 128, 4 and 8 at B = 64) on rows of 40 to
+    2190 blocks, through the register mask kernel (up to 2048 blocks) and the
+    general one (beyond), for the base and the dual-branch masks, with and
+    without the block-mask output (NULL mask: the lists alone)."""
+    announce(f"page retention nb={nb} B={block} sink={sink} local={local}")
+    rng = np.random.default_rng(nb * 10 + sink)
+    hq, gamma, gr = 2, 0.3, 0.6
+    P = np.tril(rng.random((hq, nb, nb)) ** 4).astype(np.float32)
+    Pr = np.tril(rng.random((hq, nb, nb)) ** 4).astype(np.float32)
+    seq = nb * block
+    Pt, Prt = torch.from_numpy(P).cuda(), torch.from_numpy(Pr).cuda()
+    m, idx, cnt = bsp.mask(Pt, gamma, seq, block, sink, local)
+    m0, idx0, cnt0 = bsp.mask(Pt, gamma, seq, block, sink, local, want_mask=False)
+    md, idxd, cntd = bsp.mask_dual(Pt, Prt, gamma, gr, seq, block, sink, local)
+    md0, idxd0, cntd0 = bsp.mask_dual(Pt, Prt, gamma, gr, seq, block, sink, local,
+                                      want_mask=False)
+    torch.cuda.synchronize()
+    assert m0 is None and md0 is None
+    P64, Pr64 = P.astype(np.float64), Pr.astype(np.float64)
+    om, oidx, ocnt = oracle.mask(P64, gamma, sink, local)
+    gm = m.cpu().numpy()
+    H.check_mask(gm, idx.cpu().numpy(), cnt.cpu().numpy(),
+                 dict(P=P64, mask=om, idx=oidx, cnt=ocnt), gamma, sink, local)
+    I = np.arange(nb)[:, None]
+    J = np.arange(nb)[None, :]
+    forced = (J <= I) & ((J < sink) | (I - J < local))
+    assert np.all(gm[:, forced] == 1)
+    omd, _, ocntd = oracle.mask_dual(P64, Pr64, gamma, gr, sink, local)
+    _check_dual(md.cpu().numpy(), idxd.cpu().numpy(), cntd.cpu().numpy(), P64, Pr64, gamma, gr,
+                omd, ocntd, sink, local)
+    for c1, i1, c2, i2 in ((cnt, idx, cnt0, idx0), (cntd, idxd, cntd0, idxd0)):
+        assert torch.equal(c1, c2)
+        keep = torch.arange(nb, device=c1.device)[None, None, :] < c1[..., None]
+        assert torch.equal(i1[keep], i2[keep])
+
+
+@pytest.mark.parametrize("dtype,d,block,seq,sink,local", [
+    ("bf16", 128, 128, 5000, 2, 4), ("fp8", 128, 128, 4100, 2, 4), ("bf16", 64, 64, 3000, 4, 8),
+    ("f32", 64, 64, 2000, 4, 8)])
+def test_page_retention_pipeline(dtype, d, block, seq, sink, local):
+    """Score, mask and attention with the pages' sink and window sizes on
+    generated inputs: every block of the stage 1-2 outputs, sampled rows of
+    the attention output."""
+    announce(f"page retention pipeline {dtype} d={d} B={block} seq={seq} sink={sink} "
+             f"local={local}")
+    c = gen.make_case(8, 2, seq, d, block, dtype, 500 + seq, gamma=0.2, rope=True, n_vert=6,
+                      slash=True, block_offset=1.0)
+    full_check(c, sink=sink, local=local, rows=H.sample_rows(c.hq, c.seq, c.block, n_pos=16))
 
 
 def test_gamma0_equals_dense_path_bitwise():
