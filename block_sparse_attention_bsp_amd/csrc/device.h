@@ -122,16 +122,6 @@ __device__ __forceinline__ int varlen_seq_of(const int32_t *cu_blocks, int nseq,
   return lo;
 }
 
-// Orders a wavefront's LDS accesses across its lanes: every LDS store a
-// lane issued before it is visible to the loads any lane of the same
-// wavefront issues after it (a wavefront-scope release/acquire fence, which
-// also keeps the compiler from moving LDS accesses across it).
-__device__ __forceinline__ void wave_lds_sync() {
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-  __builtin_amdgcn_wave_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-}
-
 __device__ __forceinline__ float wave_max(float v) {
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));

@@ -24,6 +24,16 @@ namespace bsp {
 
 typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
 
+// Orders a wavefront's LDS accesses across its lanes: every LDS store a
+// lane issued before it is visible to the loads any lane of the same
+// wavefront issues after it (a wavefront-scope release/acquire fence, which
+// also keeps the compiler from moving LDS accesses across it).
+__device__ __forceinline__ void wave_lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
 // A row's kept key blocks in ascending order, written to its kv_idx row.
 // Kept entry k of the row waits in slot k % 512 of the wavefront's LDS ring;
 // whenever 256 entries wait, they leave as one 1 KiB store of 16 bytes per
