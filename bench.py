@@ -74,6 +74,9 @@ def parse():
     p.add_argument("--local", type=int, default=1,
                    help="local-window blocks always kept, the diagonal included (the pages "
                         "keep 512 tokens: 4 at block 128)")
+    p.add_argument("--fused", action="store_true",
+                   help="time stages 1-2 as the one-pass bsp_score_mask instead of bsp_score + "
+                        "bsp_mask (same outputs)")
     p.add_argument("--copy-calibration", action="store_true",
                    help="also run one 1 GiB device copy (HBM counter calibration)")
     return p.parse_args()
@@ -106,16 +109,17 @@ def cpu_model() -> str:
     return "unknown"
 
 
-def scoring_bytes(hq, hkv, seq, d, block, es, kept_entries):
+def scoring_bytes(hq, hkv, seq, d, block, es, kept_entries, fused=False):
     """Minimal HBM bytes of pool + score + mask: read Q and K; write the
     fp32 block means and read them back; write P (every entry, zeros above
-    the diagonal); read P's causal half (nothing else decides the mask);
-    write the mask, the kept indices and the counts."""
+    the diagonal); read P's causal half (nothing else decides the mask, when
+    the mask is a separate pass; the one-pass form decides it as P is
+    written); write the mask, the kept indices and the counts."""
     nb = -(-seq // block)
     rd = (hq + hkv) * seq * d * es                    # read Q, K
     pooled = 2 * (hq + hkv) * nb * d * 4              # write, then read, the means
     p_wr = hq * nb * nb * 4                           # write P
-    p_rd = hq * nb * (nb + 1) // 2 * 4                # read P where J <= I
+    p_rd = 0 if fused else hq * nb * (nb + 1) // 2 * 4  # read P where J <= I
     mask = hq * nb * nb                               # write mask
     idx = kept_entries * 4 + hq * nb * 4              # write idx (kept) and counts
     return rd + pooled + p_wr + p_rd + mask + idx
@@ -327,9 +331,21 @@ def main():
     stream = torch.cuda.current_stream()
     sp = bsp._stream()
 
+    fused = um is None and a.scorer == "pooled" and not resc and a.fused
+
     def step(ev=None):
         if ev:
             ev[0].record(stream)
+        if fused:  # stages 1 and 2 in one launch pair (pool, score with threshold)
+            bsp._check(bsp.bsp_score_mask(dsc, P(q), P(k), P(qp), P(kp), P(sc), P(mk), P(idx),
+                                          P(cnt), sp))
+            if ev:
+                ev[1].record(stream)
+                ev[2].record(stream)
+            bsp._check(bsp.bsp_attn_fwd(dsc, P(q), P(k), P(v), P(idx), P(cnt), P(o), P(lse), sp))
+            if ev:
+                ev[3].record(stream)
+            return
         if um is None and a.scorer == "arith":
             bsp._check(bsp.bsp_score_arith(dsc, P(q), P(k), P(kp), P(sc), sp))
         elif um is None:
@@ -384,7 +400,7 @@ def main():
         scoring = {"scorer": "arith", "flops": f,
                    "TFLOP/s": round(f / (st_score * 1e-3) / 1e12, 3)}
     elif um is None:  # with a caller mask the scorer does not run
-        sbytes = scoring_bytes(hq, hkv, seq, d, B, es, kept_entries)
+        sbytes = scoring_bytes(hq, hkv, seq, d, B, es, kept_entries, fused=fused)
         if resc:  # K again, the means again, radii, rescue scores written and half read
             sbytes += (hkv * seq * d * es + (hq + 2 * hkv) * nb * d * 4 + 2 * hkv * nb * 4
                        + hq * nb * nb * 4 + hq * nb * (nb + 1) // 2 * 4)
@@ -428,6 +444,9 @@ def main():
         wl += f", rescue branch gamma_r {a.rescue}"
     if a.sink != 1 or a.local != 1:
         wl += f", sink {a.sink} / local {a.local} blocks"
+    if um is None and a.scorer == "pooled" and not resc:
+        wl += (", stages 1-2 as one bsp_score_mask call" if fused
+               else ", stages 1-2 as bsp_score + bsp_mask")
     out = {
         "metric": "sparse prefill-attn ms/layer + effective TFLOP/s at 128K bf16; % MFMA peak",
         "value": round(F_dense / (ms_step * 1e-3) / 1e12, 3),
@@ -439,7 +458,8 @@ def main():
         "config": {"workload": wl, "hq": hq, "hkv": hkv, "seq_len": seq, "head_dim": d,
                    "block": B, "gamma": c.gamma, "batch": 1, "parallelism": "none (1 GPU)"},
         "ms_per_layer": round(ms_step, 4),
-        "stage_ms": {"score": round(st_score, 4), "mask": round(st_mask, 4),
+        "stage_ms": ({"score_mask": round(st_score, 4)} if fused else
+                     {"score": round(st_score, 4), "mask": round(st_mask, 4)}) | {
                      "attn": round(st_attn, 4), "stat": f"median of {a.steps} steps",
                      "attn_mean": round(st_attn_mean, 4)},
         "density": round(density, 6),

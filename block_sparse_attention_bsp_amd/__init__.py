@@ -21,7 +21,8 @@ import torch
 
 __all__ = [
     "BspError", "BspDesc", "lib", "library_path", "desc", "score", "mask", "attn_fwd", "prefill",
-    "calibrate_gamma", "score_arith", "score_rescue", "mask_dual", "bsp_score", "bsp_score_arith",
+    "calibrate_gamma", "score_arith", "score_rescue", "mask_dual", "score_mask", "bsp_score",
+    "bsp_score_arith", "bsp_score_mask",
     "bsp_score_rescue", "bsp_mask", "bsp_mask_dual", "bsp_attn_fwd", "bsp_calibrate_gamma",
     "BspVarlen", "bsp_attn_fwd_varlen", "attn_fwd_varlen", "bsp_score_varlen", "bsp_mask_varlen",
     "score_varlen", "mask_varlen", "prefill_varlen",
@@ -79,6 +80,7 @@ def lib():
         vp, P = ctypes.c_void_p, ctypes.POINTER(BspDesc)
         L.bsp_score.argtypes = [P, vp, vp, vp, vp, vp, vp]
         L.bsp_mask.argtypes = [P, vp, vp, vp, vp, vp, vp]
+        L.bsp_score_mask.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp]
         L.bsp_score_arith.argtypes = [P, vp, vp, vp, vp, vp]
         L.bsp_score_rescue.argtypes = [P, vp, vp, vp, vp, vp, vp]
         L.bsp_mask_dual.argtypes = [P, vp, vp, ctypes.c_float, vp, vp, vp, vp]
@@ -90,7 +92,7 @@ def lib():
         f32 = ctypes.c_float
         L.bsp_calibrate_gamma.argtypes = [P, vp, f32, f32, vp, vp, vp, vp,
                                           ctypes.POINTER(f32), ctypes.POINTER(f32), vp]
-        for f in (L.bsp_score, L.bsp_score_arith, L.bsp_score_rescue, L.bsp_mask,
+        for f in (L.bsp_score, L.bsp_score_mask, L.bsp_score_arith, L.bsp_score_rescue, L.bsp_mask,
                   L.bsp_mask_dual, L.bsp_attn_fwd, L.bsp_attn_fwd_varlen,
                   L.bsp_calibrate_gamma, L.bsp_score_varlen, L.bsp_mask_varlen):
             f.restype = ctypes.c_int32
@@ -117,6 +119,12 @@ def _check(status: int):
 
 def bsp_score(d: BspDesc, q, k, q_pool, k_pool, score_out, stream) -> int:
     return lib().bsp_score(ctypes.byref(d), q, k, q_pool, k_pool, score_out, stream)
+
+
+def bsp_score_mask(d: BspDesc, q, k, q_pool, k_pool, score_out, mask_out, kv_idx, kv_cnt,
+                   stream) -> int:
+    return lib().bsp_score_mask(ctypes.byref(d), q, k, q_pool, k_pool, score_out, mask_out, kv_idx,
+                                kv_cnt, stream)
 
 
 def bsp_score_arith(d: BspDesc, q, k, k_pool, score_out, stream) -> int:
@@ -235,6 +243,28 @@ def score(q: torch.Tensor, k: torch.Tensor, block: int, sm_scale: float = 0.0,
     sc = torch.empty((hq, nb, nb), dtype=torch.float32, device=q.device)
     _check(bsp_score(dsc, _ptr(q), _ptr(k), _ptr(qp), _ptr(kp), _ptr(sc), _stream()))
     return qp, kp, sc
+
+
+def score_mask(q: torch.Tensor, k: torch.Tensor, block: int, gamma: float, sm_scale: float = 0.0,
+               sink_blocks: int = 1, local_blocks: int = 1, q_scale=None, k_scale=None,
+               want_mask: bool = True):
+    """Stages 1 and 2 in one pass (bsp_score_mask): the outputs of score()
+    followed by mask() without a caller mask.  Returns (q_pool, k_pool, score,
+    mask or None, kv_idx, kv_cnt)."""
+    dsc = _desc_qkv(q, k, block, gamma=gamma, sm_scale=sm_scale, sink_blocks=sink_blocks,
+                    local_blocks=local_blocks, q_scale=q_scale, k_scale=k_scale)
+    hq, seq, d = q.shape
+    nb = -(-seq // block)
+    dev = q.device
+    qp = torch.empty((hq, nb, d), dtype=torch.float32, device=dev)
+    kp = torch.empty((k.shape[0], nb, d), dtype=torch.float32, device=dev)
+    sc = torch.empty((hq, nb, nb), dtype=torch.float32, device=dev)
+    m = torch.empty((hq, nb, nb), dtype=torch.uint8, device=dev) if want_mask else None
+    idx = torch.empty((hq, nb, nb), dtype=torch.int32, device=dev)
+    cnt = torch.empty((hq, nb), dtype=torch.int32, device=dev)
+    _check(bsp_score_mask(dsc, _ptr(q), _ptr(k), _ptr(qp), _ptr(kp), _ptr(sc), _ptr(m), _ptr(idx),
+                          _ptr(cnt), _stream()))
+    return qp, kp, sc, m, idx, cnt
 
 
 def score_arith(q: torch.Tensor, k: torch.Tensor, block: int, sm_scale: float = 0.0,
@@ -508,9 +538,17 @@ def prefill_varlen(q, k_cache, v_cache, page_table, seqlens, block: int, gamma: 
 
 
 def prefill(q, k, v, block: int, gamma: float, sm_scale: float = 0.0, sink_blocks: int = 1,
-            local_blocks: int = 1, user_mask=None, q_scale=None, k_scale=None, v_scale=None):
-    """All three stages on the current stream.  Returns a dict of every output."""
+            local_blocks: int = 1, user_mask=None, q_scale=None, k_scale=None, v_scale=None,
+            fused: bool = False):
+    """All three stages on the current stream.  Returns a dict of every output.
+    fused: stages 1 and 2 as one bsp_score_mask call (same outputs)."""
     out = {}
+    if fused and user_mask is None:
+        (out["q_pool"], out["k_pool"], out["score"], m, idx, cnt) = score_mask(
+            q, k, block, gamma, sm_scale, sink_blocks, local_blocks, q_scale, k_scale)
+        o, lse = attn_fwd(q, k, v, block, idx, cnt, sm_scale, q_scale, k_scale, v_scale)
+        out.update(mask=m, kv_idx=idx, kv_cnt=cnt, o=o, lse=lse)
+        return out
     if user_mask is None:
         out["q_pool"], out["k_pool"], out["score"] = score(q, k, block, sm_scale, q_scale, k_scale)
     m, idx, cnt = mask(out.get("score"), gamma, q.shape[1], block, sink_blocks, local_blocks,

@@ -64,6 +64,26 @@ bsp_status bsp_score(const bsp_desc *desc, const void *q, const void *k, float *
   return hip_status(bsp::launch_score(s, scale_of(desc), q_pool, k_pool, nullptr, score, hs));
 }
 
+bsp_status bsp_score_mask(const bsp_desc *desc, const void *q, const void *k, float *q_pool,
+                          float *k_pool, float *score, uint8_t *mask, int32_t *kv_idx,
+                          int32_t *kv_cnt, void *stream) {
+  bsp_status st = check_desc(desc, true);
+  if (st != BSP_OK) return st;
+  if (!(desc->gamma >= 0.f && desc->gamma <= 1.f)) return BSP_ERR_BAD_VALUE;  // also NaN
+  if (desc->sink_blocks < 0 || desc->local_blocks < 0) return BSP_ERR_BAD_VALUE;
+  if (desc->seq == 0) return BSP_OK;
+  if (!q || !k || !q_pool || !k_pool || !score || !kv_idx || !kv_cnt) return BSP_ERR_NULL_POINTER;
+  const bool fp8 = desc->dtype == BSP_DTYPE_FP8_E4M3;
+  if (fp8 && (!desc->q_scale || !desc->k_scale)) return BSP_ERR_BAD_DTYPE;
+  if (!fp8 && (desc->q_scale || desc->k_scale || desc->v_scale)) return BSP_ERR_BAD_DTYPE;
+  const Shape s = shape_of(desc);
+  hipStream_t hs = (hipStream_t)stream;
+  hipError_t e = bsp::launch_pool(s, q, k, desc->q_scale, desc->k_scale, q_pool, k_pool, hs);
+  if (e != hipSuccess) return BSP_ERR_HIP;
+  const bsp::FuseMask fz{desc->gamma, desc->sink_blocks, desc->local_blocks, mask, kv_idx, kv_cnt};
+  return hip_status(bsp::launch_score_mask(s, scale_of(desc), q_pool, k_pool, score, fz, hs));
+}
+
 bsp_status bsp_score_arith(const bsp_desc *desc, const void *q, const void *k, float *k_pool,
                            float *score, void *stream) {
   bsp_status st = check_desc(desc, true);

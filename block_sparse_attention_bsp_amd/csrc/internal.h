@@ -24,6 +24,17 @@ hipError_t launch_pool(const Shape &s, const void *q, const void *k, const float
                        const float *k_scale, float *q_pool, float *k_pool, hipStream_t st);
 hipError_t launch_score(const Shape &s, float c, const float *q_pool, const float *k_pool,
                         const float *k_radius, float *score, hipStream_t st);
+// The threshold of stage 2 fused into the score kernel's second pass
+// (passed to the kernel by value): keep = P >= gamma * row max, or J < sink,
+// or I - J < local, and J <= I; mask may be null.
+struct FuseMask {
+  float gamma;
+  int sink, local;
+  uint8_t *mask;
+  int32_t *idx, *cnt;
+};
+hipError_t launch_score_mask(const Shape &s, float c, const float *q_pool, const float *k_pool,
+                             float *score, const FuseMask &fz, hipStream_t st);
 hipError_t launch_radius(const Shape &s, const void *k, const float *k_scale, const float *k_pool,
                          float *k_radius, hipStream_t st);
 hipError_t launch_score_arith(const Shape &s, float c, const void *q, const float *k_pool,

@@ -24,6 +24,7 @@
 // upper bound on the block's best per-key logit, and its row softmax.
 #include "device.h"
 #include "internal.h"
+#include "kept_list.h"
 
 namespace bsp {
 
@@ -93,12 +94,21 @@ __device__ __forceinline__ void score_half(const uint8_t *__restrict__ buf, int 
 // cost as much as pass 1.  Four wavefronts (72 KiB of staging) let two
 // workgroups share a CU, so one's loads, barriers and stores overlap the
 // other's products.
-template <int D, bool RESC, bool VEC>
+//
+// FUSE (the threshold path of stage 2 in the same launch): pass 2 also
+// decides and compacts the mask.  A row's largest P is exactly 1/L (its
+// largest raw score gives exp2(0) = 1), so the threshold gamma * max P is
+// known before the row is rewritten; each wavefront then takes whole rows,
+// writes P, the row's block mask and its ascending kept list, with the same
+// arithmetic as the mask kernel on the P it has just written, so nothing
+// reads P back.
+template <int D, bool RESC, bool VEC, bool FUSE>
 __global__ __launch_bounds__(256, 2) void score_kernel(const float *__restrict__ q_pool,
                                                        const float *__restrict__ k_pool,
                                                        const float *__restrict__ k_radius,
                                                        float *__restrict__ P, int hq, int hkv,
-                                                       int nb, float c2) {
+                                                       int nb, float c2, FuseMask fz) {
+  static_assert(!(RESC && FUSE), "the fused threshold serves the base scores");
   using S = ScoreStage<D>;
   constexpr int NWV = 4;      // wavefronts
   constexpr int NT = NWV * 64;
@@ -284,7 +294,64 @@ __global__ __launch_bounds__(256, 2) void score_kernel(const float *__restrict__
   // ---- pass 2: the group's rows in place, row-major: P = exp2(raw - M) / L
   // on the causal tiles, zeros above them
   const int jc = min(ntc * 32, nb);  // columns written in pass 1
-  if (vec) {
+  if constexpr (FUSE) {
+    // one wavefront per row; the staging buffers are idle now (every load
+    // has landed), so a wave's kept-list ring lives in its own
+    int32_t *ring = (int32_t *)&stg0[w][0];
+    for (int rr = w; rr < rows; rr += NWV) {
+      const int I = I0 + rr;
+      const float M = row_m[rr], inv = row_inv[rr];
+      const float thr = fz.gamma * inv;  // gamma times the row's largest P
+      float *prow = pgrp + (size_t)rr * nb;
+      const size_t orow = ((size_t)h * nb + I) * nb;
+      KeptList kl;
+      kl.init(ring, fz.idx + orow, lane, vec);
+      for (int J0 = 0; J0 < nb; J0 += 2048) {
+        float x[8][4];  // raw scores: a whole row of up to 2048 blocks in flight
+#pragma unroll
+        for (int c = 0; c < 8; ++c) {
+          const int J = J0 + c * 256 + 4 * lane;
+          if (vec && J < jc) {  // jc % 4 == 0 here: J .. J + 3 all below it
+            const float4 t = *(const float4 *)(prow + J);
+            x[c][0] = t.x; x[c][1] = t.y; x[c][2] = t.z; x[c][3] = t.w;
+          } else {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) x[c][e] = J + e < jc ? prow[J + e] : -INFINITY;
+          }
+        }
+#pragma unroll
+        for (int c = 0; c < 8; ++c) {
+          if (J0 + c * 256 >= nb) break;
+          const int J = J0 + c * 256 + 4 * lane;
+          float pv4[4];
+          bool keep[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int Je = J + e;
+            pv4[e] = J + e < jc ? __builtin_amdgcn_exp2f(x[c][e] - M) * inv : 0.f;
+            keep[e] = Je <= I && (pv4[e] >= thr || Je < fz.sink || I - Je < fz.local);
+          }
+          if (vec && J + 3 < nb) {
+            *(float4 *)(prow + J) = make_float4(pv4[0], pv4[1], pv4[2], pv4[3]);
+            if (fz.mask)
+              *(uint32_t *)(fz.mask + orow + J) =
+                  (uint32_t)keep[0] | ((uint32_t)keep[1] << 8) | ((uint32_t)keep[2] << 16) |
+                  ((uint32_t)keep[3] << 24);
+          } else {
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+              if (J + e < nb) {
+                prow[J + e] = pv4[e];
+                if (fz.mask) fz.mask[orow + J + e] = keep[e] ? 1 : 0;
+              }
+          }
+          kl.push(keep, J);
+        }
+      }
+      const int n = kl.finish();
+      if (lane == 0) fz.cnt[(size_t)h * nb + I] = n;
+    }
+  } else if (vec) {
     const int n4 = nb / 4, c4 = jc / 4;
     constexpr int U = 8;  // loads in flight per thread
     for (int e0 = threadIdx.x; e0 < rows * n4; e0 += U * NT) {
@@ -317,17 +384,17 @@ __global__ __launch_bounds__(256, 2) void score_kernel(const float *__restrict__
   }
 }
 
-template <int D, bool RESC>
+template <int D, bool RESC, bool FUSE>
 static hipError_t launch_score_t(const Shape &s, float c, const float *qp, const float *kp,
-                                 const float *kr, float *S, hipStream_t st) {
+                                 const float *kr, float *S, const FuseMask &fz, hipStream_t st) {
   // heaviest row groups of every head first
   const dim3 grid(s.hq, (s.nb + 31) / 32);
   if (s.nb % 4 == 0)
-    hipLaunchKernelGGL((score_kernel<D, RESC, true>), grid, dim3(256), 0, st, qp, kp, kr, S, s.hq,
-                       s.hkv, s.nb, c * kLog2e);
+    hipLaunchKernelGGL((score_kernel<D, RESC, true, FUSE>), grid, dim3(256), 0, st, qp, kp, kr,
+                       S, s.hq, s.hkv, s.nb, c * kLog2e, fz);
   else
-    hipLaunchKernelGGL((score_kernel<D, RESC, false>), grid, dim3(256), 0, st, qp, kp, kr, S,
-                       s.hq, s.hkv, s.nb, c * kLog2e);
+    hipLaunchKernelGGL((score_kernel<D, RESC, false, FUSE>), grid, dim3(256), 0, st, qp, kp, kr,
+                       S, s.hq, s.hkv, s.nb, c * kLog2e, fz);
   return hipGetLastError();
 }
 
@@ -395,12 +462,19 @@ hipError_t launch_score_varlen(const Shape &s, const VarlenArgs &vl, float c, co
 
 hipError_t launch_score(const Shape &s, float c, const float *q_pool, const float *k_pool,
                         const float *k_radius, float *S, hipStream_t st) {
+  const FuseMask none{};
   if (k_radius) {
-    if (s.d == 64) return launch_score_t<64, true>(s, c, q_pool, k_pool, k_radius, S, st);
-    return launch_score_t<128, true>(s, c, q_pool, k_pool, k_radius, S, st);
+    if (s.d == 64) return launch_score_t<64, true, false>(s, c, q_pool, k_pool, k_radius, S, none, st);
+    return launch_score_t<128, true, false>(s, c, q_pool, k_pool, k_radius, S, none, st);
   }
-  if (s.d == 64) return launch_score_t<64, false>(s, c, q_pool, k_pool, nullptr, S, st);
-  return launch_score_t<128, false>(s, c, q_pool, k_pool, nullptr, S, st);
+  if (s.d == 64) return launch_score_t<64, false, false>(s, c, q_pool, k_pool, nullptr, S, none, st);
+  return launch_score_t<128, false, false>(s, c, q_pool, k_pool, nullptr, S, none, st);
+}
+
+hipError_t launch_score_mask(const Shape &s, float c, const float *q_pool, const float *k_pool,
+                             float *S, const FuseMask &fz, hipStream_t st) {
+  if (s.d == 64) return launch_score_t<64, false, true>(s, c, q_pool, k_pool, nullptr, S, fz, st);
+  return launch_score_t<128, false, true>(s, c, q_pool, k_pool, nullptr, S, fz, st);
 }
 
 }  // namespace bsp

@@ -47,7 +47,7 @@
 extern "C" {
 #endif
 
-#define BSP_ABI_VERSION 6
+#define BSP_ABI_VERSION 7
 
 typedef enum bsp_status {
   BSP_OK = 0,
@@ -153,6 +153,23 @@ bsp_status bsp_score_arith(const bsp_desc *desc, const void *q, const void *k, f
  */
 bsp_status bsp_mask(const bsp_desc *desc, const float *score, const uint8_t *user_mask,
                     uint8_t *mask, int32_t *kv_idx, int32_t *kv_cnt, void *stream);
+
+/*
+ * bsp_score_mask - stages 1 and 2 (threshold path) in one pass: exactly
+ * bsp_score followed by bsp_mask without a caller mask, every output bit for
+ * bit the same (FlashPrefill summary page, section 3 "Max-based Dynamic
+ * Thresholding": the threshold is gamma times the row's peak score, which
+ * the score pass already holds when it normalises a row: the peak of P is
+ * 1 / (the row's sum of exp), so the mask is decided as P is written and P
+ * is never read back; Appendix B: the three stages in order).
+ *
+ * q, k, q_pool, k_pool, score: as for bsp_score (all written)
+ * mask, kv_idx, kv_cnt:        as for bsp_mask (mask may be NULL)
+ * Reads desc->gamma, sink_blocks and local_blocks like bsp_mask.
+ */
+bsp_status bsp_score_mask(const bsp_desc *desc, const void *q, const void *k, float *q_pool,
+                          float *k_pool, float *score, uint8_t *mask, int32_t *kv_idx,
+                          int32_t *kv_cnt, void *stream);
 
 /*
  * bsp_score_rescue - rescue branch of the scores (thelatestinai page,

@@ -29,7 +29,7 @@ def built():
 def test_header_declares_the_entry_points():
     assert _declared() == ["bsp_abi_version", "bsp_attn_fwd", "bsp_attn_fwd_varlen",
                            "bsp_calibrate_gamma", "bsp_mask", "bsp_mask_dual", "bsp_mask_varlen",
-                           "bsp_score", "bsp_score_arith", "bsp_score_rescue",
+                           "bsp_score", "bsp_score_arith", "bsp_score_mask", "bsp_score_rescue",
                            "bsp_score_varlen", "bsp_status_string"]
 
 
@@ -118,6 +118,20 @@ def test_empty_sequence_is_a_no_op():
     assert bsp.bsp_score(_d(seq=0), FAKE, FAKE, FAKE, FAKE, FAKE, None) == 0
     assert bsp.bsp_mask(_d(seq=0), FAKE, None, None, FAKE, FAKE, None) == 0
     assert bsp.bsp_attn_fwd(_d(seq=0), FAKE, FAKE, FAKE, None, None, FAKE, None, None) == 0
+
+
+def test_score_mask_host_checks():
+    sm = lambda d, *p: bsp.bsp_score_mask(d, *p, None)
+    full = (FAKE,) * 8
+    assert sm(_d(gamma=1.5), *full) == 4
+    assert sm(_d(gamma=float("nan")), *full) == 4
+    assert sm(_d(sink_blocks=-1), *full) == 4
+    assert sm(_d(), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE) == 1  # kv_idx
+    assert sm(_d(), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None) == 1  # kv_cnt
+    assert sm(_d(), FAKE, FAKE, FAKE, FAKE, None, FAKE, FAKE, FAKE) == 1  # score
+    assert sm(_d(dtype=bsp.DTYPE_FP8_E4M3), *full) == 3                 # no fp8 scales
+    assert sm(_d(d=96), *full) == 2
+    assert sm(_d(seq=0), *((None,) * 8)) == 0
 
 
 def test_python_layer_raises_bsp_error():

@@ -74,6 +74,9 @@ def test_scoring_bytes_at_128k_equal_the_three_kernels_algorithmic_bytes(bench):
     assert got == pool + score + mask == 1686372352
     assert round(pool / 1e9, 3) == 1.363 and round(score / 1e9, 3) == 0.155
     assert round(mask / 1e9, 3) == 0.168
+    # the one-pass form decides the mask as P is written: no read of P's causal half
+    fused = bench.scoring_bytes(hq, hkv, seq, d, B, 2, hq * causal, fused=True)
+    assert got - fused == hq * causal * 4
 
 
 def test_traffic_is_reported_only_for_the_counted_sources(bench, tmp_path, monkeypatch):

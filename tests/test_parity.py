@@ -627,6 +627,49 @@ def test_page_retention_pipeline(dtype, d, block, seq, sink, local):
     full_check(c, sink=sink, local=local, rows=H.sample_rows(c.hq, c.seq, c.block, n_pos=16))
 
 
+def _equal_lists(c1, i1, c2, i2, nb):
+    assert torch.equal(c1, c2)
+    keep = torch.arange(nb, device=c1.device)[None, None, :] < c1[..., None]
+    assert torch.equal(i1[keep], i2[keep])
+
+
+@pytest.mark.parametrize("dtype,d,block,hq,hkv,seq,gamma,sink,local", [
+    ("bf16", 128, 128, 8, 2, 1000, 0.2, 1, 1), ("bf16", 64, 64, 8, 2, 777, 0.2, 4, 8),
+    ("fp8", 128, 128, 8, 2, 1000, 0.3, 2, 4), ("fp8", 64, 64, 6, 3, 700, 0.2, 1, 1),
+    ("f32", 128, 64, 4, 2, 333, 0.2, 1, 1), ("f32", 64, 128, 4, 1, 250, 0.0, 0, 0),
+    ("bf16", 64, 64, 2, 1, 1022 * 64 - 5, 0.2, 1, 1), ("bf16", 64, 64, 2, 1, 2047 * 64, 0.1, 4, 8),
+    ("bf16", 64, 64, 2, 1, 2190 * 64, 0.2, 2, 4), ("bf16", 128, 128, 4, 2, 1024 * 128, 1.0, 1, 1),
+])
+def test_score_mask_equals_score_then_mask(dtype, d, block, hq, hkv, seq, gamma, sink, local):
+    """bsp_score_mask writes exactly what bsp_score followed by bsp_mask
+    writes (block means, scores, mask, kv lists and counts, bit for bit),
+    with and without the block-mask output; rows of 4 to 2190 blocks, rows
+    whose length is not a multiple of 4, the pages' sink and window."""
+    announce(f"score_mask {dtype} d={d} B={block} heads {hq}/{hkv} seq={seq} gamma={gamma} "
+             f"sink={sink} local={local}")
+    c = gen.make_case(hq, hkv, seq, d, block, dtype, 900 + seq % 1000, gamma=gamma, rope=True,
+                      n_vert=6, slash=True, block_offset=1.0)
+    dv = H.dev(c)
+    kw = dict(q_scale=dv["q_scale"], k_scale=dv["k_scale"])
+    qp, kp, sc = bsp.score(dv["q"], dv["k"], block, **kw)
+    m, idx, cnt = bsp.mask(sc, gamma, seq, block, sink, local)
+    qp2, kp2, sc2, m2, idx2, cnt2 = bsp.score_mask(dv["q"], dv["k"], block, gamma,
+                                                   sink_blocks=sink, local_blocks=local, **kw)
+    r3 = bsp.score_mask(dv["q"], dv["k"], block, gamma, sink_blocks=sink, local_blocks=local,
+                        want_mask=False, **kw)
+    torch.cuda.synchronize()
+    assert r3[3] is None
+    for a, b in ((qp, qp2), (kp, kp2), (sc, sc2), (m, m2), (sc, r3[2])):
+        assert torch.equal(a, b)
+    _equal_lists(cnt, idx, cnt2, idx2, c.nb)
+    _equal_lists(cnt, idx, r3[5], r3[4], c.nb)
+    if c.nb <= 1024:  # the mask against the oracle (larger rows: the long-row tests)
+        orc = oracle.prefill(c, gamma, sink_blocks=sink, local_blocks=local, with_attn=False)
+        nband = H.check_mask(m2.cpu().numpy(), idx2.cpu().numpy(), cnt2.cpu().numpy(), orc, gamma,
+                             sink, local)
+        print(f"  band blocks {nband}", flush=True)
+
+
 def test_gamma0_equals_dense_path_bitwise():
     announce("gamma=0 vs dense")
     c = gen.make_case(4, 2, 1024, 128, 128, "bf16", 5, rope=True, n_vert=4)

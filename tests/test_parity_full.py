@@ -102,3 +102,25 @@ def test_sparse_caller_mask_full_size_128k():
     print(f"  generated in {time.time() - t0:.1f}s", flush=True)
     dens = _full_size_check(c, 33, user_mask=um, t0=t0)
     assert dens < 0.05
+
+
+@pytest.mark.parametrize("which", ["config3", "config4", "s2_config3"])
+def test_score_mask_full_size_equals_two_calls(which):
+    """The one-pass score and mask at the measured sizes (128K bf16, 256K
+    fp8 with 2048-block rows, and the pruning 128K layer) writes what
+    bsp_score followed by bsp_mask writes, bit for bit."""
+    t0 = time.time()
+    print(f"\n[case] score_mask vs score + mask, {which}", flush=True)
+    c = gen.make_s2(3) if which.startswith("s2") else gen.make_config(int(which[-1]))
+    dv = H.dev(c)
+    kw = dict(q_scale=dv["q_scale"], k_scale=dv["k_scale"])
+    qp, kp, sc = bsp.score(dv["q"], dv["k"], c.block, **kw)
+    m, idx, cnt = bsp.mask(sc, c.gamma, c.seq, c.block)
+    r = bsp.score_mask(dv["q"], dv["k"], c.block, c.gamma, **kw)
+    torch.cuda.synchronize()
+    for a, b in ((qp, r[0]), (kp, r[1]), (sc, r[2]), (m, r[3]), (cnt, r[5])):
+        assert torch.equal(a, b)
+    keep = torch.arange(c.nb, device=cnt.device)[None, None, :] < cnt[..., None]
+    assert torch.equal(idx[keep], r[4][keep])
+    dens = cnt.sum().item() / (c.hq * c.nb * (c.nb + 1) / 2)
+    print(f"  density {dens:.4f} total {time.time() - t0:.1f}s", flush=True)
