@@ -77,6 +77,9 @@ def parse():
     p.add_argument("--fused", action="store_true",
                    help="time stages 1-2 as the one-pass bsp_score_mask instead of bsp_score + "
                         "bsp_mask (same outputs)")
+    p.add_argument("--no-widen", action="store_true",
+                   help="e4m3 inputs: attend on the V codes instead of widening V to bf16 first "
+                        "(bsp_widen_e4m3, then BSP_DTYPE_FP8_E4M3_V_BF16; same outputs)")
     p.add_argument("--copy-calibration", action="store_true",
                    help="also run one 1 GiB device copy (HBM counter calibration)")
     return p.parse_args()
@@ -327,11 +330,27 @@ def main():
     lse = torch.empty((hq, seq), dtype=f32, device=dev)
     dsc = bsp.desc(hq, hkv, seq, d, B, {"f32": 0, "bf16": 1, "fp8": 2}[c.dtype], gamma=c.gamma,
                    sink_blocks=a.sink, local_blocks=a.local, q_scale=qs, k_scale=ks, v_scale=vs)
+    # e4m3: V widened to bf16 once per step, then attention on the mixed dtype
+    widen = c.dtype == "fp8" and not a.no_widen
+    vw = torch.empty((hkv, seq, d), dtype=torch.bfloat16, device=dev) if widen else None
+    dsc_attn = (bsp.desc(hq, hkv, seq, d, B, bsp.DTYPE_FP8_E4M3_V_BF16, q_scale=qs, k_scale=ks,
+                         v_scale=vs) if widen else dsc)
+    v_attn = vw if widen else v
     P = bsp._ptr
     stream = torch.cuda.current_stream()
     sp = bsp._stream()
 
     fused = um is None and a.scorer == "pooled" and not resc and a.fused
+
+    def attend(ev):
+        if widen:
+            bsp._check(bsp.bsp_widen_e4m3(P(v), P(vw), v.numel(), sp))
+        if ev:
+            ev[3].record(stream)
+        bsp._check(bsp.bsp_attn_fwd(dsc_attn, P(q), P(k), P(v_attn), P(idx), P(cnt), P(o), P(lse),
+                                    sp))
+        if ev:
+            ev[4].record(stream)
 
     def step(ev=None):
         if ev:
@@ -342,9 +361,7 @@ def main():
             if ev:
                 ev[1].record(stream)
                 ev[2].record(stream)
-            bsp._check(bsp.bsp_attn_fwd(dsc, P(q), P(k), P(v), P(idx), P(cnt), P(o), P(lse), sp))
-            if ev:
-                ev[3].record(stream)
+            attend(ev)
             return
         if um is None and a.scorer == "arith":
             bsp._check(bsp.bsp_score_arith(dsc, P(q), P(k), P(kp), P(sc), sp))
@@ -361,14 +378,12 @@ def main():
                                     P(cnt), sp))
         if ev:
             ev[2].record(stream)
-        bsp._check(bsp.bsp_attn_fwd(dsc, P(q), P(k), P(v), P(idx), P(cnt), P(o), P(lse), sp))
-        if ev:
-            ev[3].record(stream)
+        attend(ev)
 
     for _ in range(a.warmup):
         step()
     torch.cuda.synchronize()
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(a.steps)]
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(a.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(a.steps):
@@ -380,8 +395,9 @@ def main():
     # stream the kernels run on)
     st_score = float(np.median([e[0].elapsed_time(e[1]) for e in evs]))
     st_mask = float(np.median([e[1].elapsed_time(e[2]) for e in evs]))
-    st_attn = float(np.median([e[2].elapsed_time(e[3]) for e in evs]))
-    st_attn_mean = float(np.mean([e[2].elapsed_time(e[3]) for e in evs]))
+    st_widen = float(np.median([e[2].elapsed_time(e[3]) for e in evs]))
+    st_attn = float(np.median([e[3].elapsed_time(e[4]) for e in evs]))
+    st_attn_mean = float(np.mean([e[3].elapsed_time(e[4]) for e in evs]))
 
     cnt_h = cnt.cpu().numpy()
     kept_entries = int(cnt_h.sum())
@@ -447,6 +463,8 @@ def main():
     if um is None and a.scorer == "pooled" and not resc:
         wl += (", stages 1-2 as one bsp_score_mask call" if fused
                else ", stages 1-2 as bsp_score + bsp_mask")
+    if widen:
+        wl += ", V widened to bf16 in the step (bsp_widen_e4m3) before attention"
     out = {
         "metric": "sparse prefill-attn ms/layer + effective TFLOP/s at 128K bf16; % MFMA peak",
         "value": round(F_dense / (ms_step * 1e-3) / 1e12, 3),
@@ -459,7 +477,8 @@ def main():
                    "block": B, "gamma": c.gamma, "batch": 1, "parallelism": "none (1 GPU)"},
         "ms_per_layer": round(ms_step, 4),
         "stage_ms": ({"score_mask": round(st_score, 4)} if fused else
-                     {"score": round(st_score, 4), "mask": round(st_mask, 4)}) | {
+                     {"score": round(st_score, 4), "mask": round(st_mask, 4)}) |
+                    ({"widen": round(st_widen, 4)} if widen else {}) | {
                      "attn": round(st_attn, 4), "stat": f"median of {a.steps} steps",
                      "attn_mean": round(st_attn_mean, 4)},
         "density": round(density, 6),

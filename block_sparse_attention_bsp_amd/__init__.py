@@ -26,14 +26,14 @@ __all__ = [
     "bsp_score_rescue", "bsp_mask", "bsp_mask_dual", "bsp_attn_fwd", "bsp_calibrate_gamma",
     "BspVarlen", "bsp_attn_fwd_varlen", "attn_fwd_varlen", "bsp_score_varlen", "bsp_mask_varlen",
     "score_varlen", "mask_varlen", "prefill_varlen",
-    "bsp_status_string", "bsp_abi_version",
-    "DTYPE_F32", "DTYPE_BF16", "DTYPE_FP8_E4M3",
+    "bsp_status_string", "bsp_abi_version", "bsp_widen_e4m3", "widen_e4m3",
+    "DTYPE_F32", "DTYPE_BF16", "DTYPE_FP8_E4M3", "DTYPE_FP8_E4M3_V_BF16",
 ]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
 library_path = os.path.join(_PKG, "libbsp.so")
 
-DTYPE_F32, DTYPE_BF16, DTYPE_FP8_E4M3 = 0, 1, 2
+DTYPE_F32, DTYPE_BF16, DTYPE_FP8_E4M3, DTYPE_FP8_E4M3_V_BF16 = 0, 1, 2, 3
 _STATUS = {0: "BSP_OK", 1: "BSP_ERR_NULL_POINTER", 2: "BSP_ERR_BAD_SHAPE", 3: "BSP_ERR_BAD_DTYPE",
            4: "BSP_ERR_BAD_VALUE", 5: "BSP_ERR_UNSUPPORTED", 6: "BSP_ERR_HIP"}
 
@@ -89,12 +89,14 @@ def lib():
                                           vp, vp]
         L.bsp_score_varlen.argtypes = [P, ctypes.POINTER(BspVarlen), vp, vp, vp, vp, vp, vp]
         L.bsp_mask_varlen.argtypes = [P, ctypes.POINTER(BspVarlen), vp, vp, vp, vp, vp, vp]
+        L.bsp_widen_e4m3.argtypes = [vp, vp, ctypes.c_int64, vp]
         f32 = ctypes.c_float
         L.bsp_calibrate_gamma.argtypes = [P, vp, f32, f32, vp, vp, vp, vp,
                                           ctypes.POINTER(f32), ctypes.POINTER(f32), vp]
         for f in (L.bsp_score, L.bsp_score_mask, L.bsp_score_arith, L.bsp_score_rescue, L.bsp_mask,
                   L.bsp_mask_dual, L.bsp_attn_fwd, L.bsp_attn_fwd_varlen,
-                  L.bsp_calibrate_gamma, L.bsp_score_varlen, L.bsp_mask_varlen):
+                  L.bsp_calibrate_gamma, L.bsp_score_varlen, L.bsp_mask_varlen,
+                  L.bsp_widen_e4m3):
             f.restype = ctypes.c_int32
         L.bsp_status_string.argtypes = [ctypes.c_int32]
         L.bsp_status_string.restype = ctypes.c_char_p
@@ -174,6 +176,10 @@ def bsp_mask_varlen(d: BspDesc, vl: BspVarlen, score_in, user_mask, mask_out, kv
                                  kv_idx, kv_cnt, stream)
 
 
+def bsp_widen_e4m3(src, dst, n: int, stream) -> int:
+    return lib().bsp_widen_e4m3(src, dst, n, stream)
+
+
 # ---------------------------------------------------------------- torch level
 def _dtype_code(t: torch.Tensor) -> int:
     if t.dtype == torch.float32:
@@ -215,21 +221,40 @@ def _shape(t: Optional[torch.Tensor], want, name: str):
         raise BspError(2, f"{name} has shape {tuple(t.shape)}, expected {tuple(want)}")
 
 
+def _is_e4m3(t: torch.Tensor) -> bool:
+    return t.dtype in (torch.uint8, torch.float8_e4m3fn)
+
+
 def _desc_qkv(q, k, block, v=None, **kw):
     if q.dim() != 3 or k.dim() != 3:
         raise BspError(2, "q and k must be [heads, seq, d]")
     hq, seq, d = q.shape
     _shape(k, (k.shape[0], seq, d), "k")
     _shape(v, k.shape, "v")
-    for t in (k, v):
+    # e4m3 Q and K may come with V already widened to bf16 (widen_e4m3)
+    v_wide = v is not None and _is_e4m3(q) and v.dtype == torch.bfloat16
+    for t in (k, None if v_wide else v):
         if t is not None and t.dtype != q.dtype:
-            raise BspError(3, "q, k and v must share one dtype")
+            raise BspError(3, "q, k and v must share one dtype (or v bf16 with e4m3 q and k)")
     for name, want in (("q_scale", hq), ("k_scale", k.shape[0]), ("v_scale", k.shape[0])):
         t = kw.get(name)
         _shape(t, (want,), name)
         if t is not None and t.dtype != torch.float32:
             raise BspError(3, f"{name} must be float32")
-    return desc(hq, k.shape[0], seq, d, block, _dtype_code(q), **kw)
+    code = DTYPE_FP8_E4M3_V_BF16 if v_wide else _dtype_code(q)
+    return desc(hq, k.shape[0], seq, d, block, code, **kw)
+
+
+def widen_e4m3(x: torch.Tensor, out=None) -> torch.Tensor:
+    """bsp_widen_e4m3: the exact bf16 values of e4m3 codes (scales not applied)."""
+    if not _is_e4m3(x):
+        raise BspError(3, "widen_e4m3 takes e4m3 codes (uint8 or float8_e4m3fn)")
+    if out is None:
+        out = torch.empty(x.shape, dtype=torch.bfloat16, device=x.device)
+    elif tuple(out.shape) != tuple(x.shape) or out.dtype != torch.bfloat16:
+        raise BspError(2, "out must be bf16 of the input's shape")
+    _check(bsp_widen_e4m3(_ptr(x), _ptr(out), x.numel(), _stream()))
+    return out
 
 
 def score(q: torch.Tensor, k: torch.Tensor, block: int, sm_scale: float = 0.0,
@@ -494,8 +519,9 @@ def attn_fwd_varlen(q, k_cache, v_cache, page_table, seqlens, block: int, kv_idx
     _varlen_cache(q, k_cache, page_table, nbs, block)
     _shape(v_cache, k_cache.shape, "v_cache")
     hkv = k_cache.shape[1]
-    if v_cache.dtype != q.dtype:
-        raise BspError(3, "q and the caches must share one dtype")
+    v_wide = _is_e4m3(q) and v_cache.dtype == torch.bfloat16
+    if k_cache.dtype != q.dtype or (v_cache.dtype != q.dtype and not v_wide):
+        raise BspError(3, "q and the caches must share one dtype (or a bf16 v_cache with e4m3)")
     stride = 1
     if kv_idx is not None:
         if kv_idx.dim() != 3 or kv_idx.shape[:2] != (hq, tb) or kv_idx.dtype != torch.int32:
@@ -507,8 +533,8 @@ def attn_fwd_varlen(q, k_cache, v_cache, page_table, seqlens, block: int, kv_idx
     for name, t, want in (("q_scale", q_scale, hq), ("k_scale", k_scale, hkv),
                           ("v_scale", v_scale, hkv)):
         _shape(t, (want,), name)
-    dsc = desc(hq, hkv, ntok, d, block, _dtype_code(q), sm_scale=sm_scale, q_scale=q_scale,
-               k_scale=k_scale, v_scale=v_scale)
+    dsc = desc(hq, hkv, ntok, d, block, DTYPE_FP8_E4M3_V_BF16 if v_wide else _dtype_code(q),
+               sm_scale=sm_scale, q_scale=q_scale, k_scale=k_scale, v_scale=v_scale)
     if block_order is not None:
         _shape(block_order, (tb,), "block_order")
         if block_order.dtype != torch.int32:
@@ -539,10 +565,14 @@ def prefill_varlen(q, k_cache, v_cache, page_table, seqlens, block: int, gamma: 
 
 def prefill(q, k, v, block: int, gamma: float, sm_scale: float = 0.0, sink_blocks: int = 1,
             local_blocks: int = 1, user_mask=None, q_scale=None, k_scale=None, v_scale=None,
-            fused: bool = False):
+            fused: bool = False, widen_v: bool = True):
     """All three stages on the current stream.  Returns a dict of every output.
-    fused: stages 1 and 2 as one bsp_score_mask call (same outputs)."""
+    fused: stages 1 and 2 as one bsp_score_mask call (same outputs).
+    widen_v: for e4m3 codes, widen V to bf16 first (bsp_widen_e4m3; the
+    outputs are bit-identical, the attention launch faster)."""
     out = {}
+    if widen_v and _is_e4m3(v):
+        v = widen_e4m3(v)
     if fused and user_mask is None:
         (out["q_pool"], out["k_pool"], out["score"], m, idx, cnt) = score_mask(
             q, k, block, gamma, sm_scale, sink_blocks, local_blocks, q_scale, k_scale)

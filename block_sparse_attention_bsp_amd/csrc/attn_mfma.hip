@@ -100,15 +100,18 @@ __device__ __forceinline__ int v_chunk(int r, int c) {
 
 
 
-template <int DT, int D, int BLK>
+// V16: V is stored as bf16 (always for bf16; for e4m3 Q/K when the caller
+// passes V already widened), so it reaches LDS by the same direct loads as K.
+template <int DT, int D, int BLK, bool V16>
 struct Attn {
+  static_assert(DT == kFP8 || V16, "bf16 inputs store V as bf16");
   using C = AttnCfg<DT, D, BLK>;
   static constexpr int RB = C::RB, LB = C::LB, DK = C::DK, KT = C::KT;
   static constexpr int NKT = C::NKT, NJ = C::NJ, NDT = C::NDT, NSUB = C::NSUB, NW = C::NW,
                        NT = C::NT;
   static constexpr int KPW = C::KCH / NW;               // K DMA chunks per wave
   static constexpr int VPW = (C::VBYTES / 16) / NW;     // V DMA chunks per wave (bf16)
-  static constexpr int VPER = C::VCHK / NT > 0 ? C::VCHK / NT : 1;  // fp8 V chunks per thread
+  static constexpr int VPER = C::VCHK / NT > 0 ? C::VCHK / NT : 1;  // e4m3 V chunks per thread
   typedef typename std::conditional<DT == kFP8, i32x8, bf16x8>::type frag_t;
 
   const uint8_t *k, *v;
@@ -123,10 +126,10 @@ struct Attn {
   f32x4 oacc[NDT][2];
   float m_used[2], l[2];
   // per-lane byte offsets (loop constants)
-  uint32_t kdma[KPW / 64], vdma[DT == kBF16 ? VPW / 64 : 1];
-  int krow[KPW / 64], vrow[DT == kBF16 ? VPW / 64 : 1];
+  uint32_t kdma[KPW / 64], vdma[V16 ? VPW / 64 : 1];
+  int krow[KPW / 64], vrow[V16 ? VPW / 64 : 1];
   int koff[DK], voff[NDT];
-  uint4 vreg[VPER];
+  uint4 vreg[V16 ? 1 : VPER];
 
   __device__ __forceinline__ void setup() {
 #pragma unroll
@@ -137,7 +140,7 @@ struct Attn {
       kdma[it] = r * RB + c * 16;
       krow[it] = r;
     }
-    if constexpr (DT == kBF16) {
+    if constexpr (V16) {
 #pragma unroll
       for (int it = 0; it < VPW / 64; ++it) {
         const int p = w * VPW + it * 64 + lane;
@@ -163,8 +166,8 @@ struct Attn {
 
   // Rows [r0, r0 + KT) of a K/V region -> LDS buffers, issued one sub-tile
   // ahead.  kr / vr describe the region (one kv head's sequence, or one cache
-  // page), vb is its V base for fp8, lim the number of valid rows in it.  K
-  // (and bf16 V) go straight to LDS; fp8 V comes back in registers for
+  // page), vb is its V base for e4m3 V, lim the number of valid rows in it.
+  // K (and bf16 V) go straight to LDS; e4m3 V comes back in registers for
   // widening.
   __device__ __forceinline__ void issue_rows(__amdgpu_buffer_rsrc_t kr, __amdgpu_buffer_rsrc_t vr,
                                              const uint8_t *vb, int r0, int lim, uint8_t *Kb,
@@ -173,7 +176,7 @@ struct Attn {
     if (r0 + KT <= lim) {
 #pragma unroll
       for (int it = 0; it < KPW / 64; ++it) lds_dma16(kr, kdma[it], ksoff, Kb + (w * KPW + it * 64) * 16);
-      if constexpr (DT == kBF16) {
+      if constexpr (V16) {
 #pragma unroll
         for (int it = 0; it < VPW / 64; ++it)
           lds_dma16(vr, vdma[it], vsoff, (uint8_t *)Vb + (w * VPW + it * 64) * 16);
@@ -185,14 +188,14 @@ struct Attn {
       for (int it = 0; it < KPW / 64; ++it)
         lds_dma16(kr, kdma[it] - (uint32_t)max(0, r0 + krow[it] - (lim - 1)) * RB, ksoff,
                   Kb + (w * KPW + it * 64) * 16);
-      if constexpr (DT == kBF16) {
+      if constexpr (V16) {
 #pragma unroll
         for (int it = 0; it < VPW / 64; ++it)
           lds_dma16(vr, vdma[it] - (uint32_t)max(0, r0 + vrow[it] - (lim - 1)) * (D * 2), vsoff,
                     (uint8_t *)Vb + (w * VPW + it * 64) * 16);
       }
     }
-    if constexpr (DT == kFP8) {
+    if constexpr (!V16) {
 #pragma unroll
       for (int it = 0; it < VPER; ++it) {
         const int e = threadIdx.x + it * NT;
@@ -205,12 +208,12 @@ struct Attn {
 
   // Sub-tile (J, sub) of this kv head's contiguous K/V
   __device__ __forceinline__ void issue(int J, int sub, uint8_t *Kb, uint16_t *Vb) {
-    issue_rows(krs, vrs, v + kvrow0 * RB, J * BLK + sub * KT, seq, Kb, Vb);
+    issue_rows(krs, vrs, v + kvrow0 * (V16 ? D * 2 : RB), J * BLK + sub * KT, seq, Kb, Vb);
   }
 
-  // fp8 only: widen the prefetched V codes to bf16 into the LDS buffer.
+  // e4m3 V only: widen the prefetched V codes to bf16 into the LDS buffer.
   __device__ __forceinline__ void store_v(uint16_t *Vb) {
-    if constexpr (DT == kFP8) {
+    if constexpr (!V16) {
 #pragma unroll
       for (int it = 0; it < VPER; ++it) {
         const int e = threadIdx.x + it * NT;
@@ -372,14 +375,14 @@ struct Attn {
   }
 };
 
-template <int DT, int D, int BLK, bool VL>
+template <int DT, int D, int BLK, bool VL, bool V16>
 __global__ __launch_bounds__(BLK * 2, (BLK == 64 && D == 128) ? 1 : 2) void attn_mfma_kernel(
     const uint8_t *__restrict__ q, const uint8_t *__restrict__ k, const uint8_t *__restrict__ v,
     const int32_t *__restrict__ kv_idx, const int32_t *__restrict__ kv_cnt,
     uint16_t *__restrict__ o, float *__restrict__ lse, const float *__restrict__ q_scale,
     const float *__restrict__ k_scale, const float *__restrict__ v_scale, int hq, int hkv,
     int seq, int nb, float sm_scale_log2, int xcd_map, VarlenArgs vl) {
-  using A = Attn<DT, D, BLK>;
+  using A = Attn<DT, D, BLK, V16>;
   using C = typename A::C;
   constexpr int RB = C::RB, LB = C::LB, DK = C::DK, KT = C::KT, NSUB = C::NSUB;
   __shared__ __attribute__((aligned(16))) uint8_t Ks0[C::KBYTES];
@@ -411,11 +414,10 @@ __global__ __launch_bounds__(BLK * 2, (BLK == 64 && D == 128) ? 1 : 2) void attn
   T.kvrow0 = (size_t)g * seq;
   if constexpr (!VL) {
     T.krs = make_rsrc(k + T.kvrow0 * RB, (uint32_t)seq * RB);
-    T.vrs = make_rsrc(v + T.kvrow0 * (DT == kBF16 ? D * 2 : RB),
-                      (uint32_t)seq * (DT == kBF16 ? D * 2 : RB));
+    T.vrs = make_rsrc(v + T.kvrow0 * (V16 ? D * 2 : RB), (uint32_t)seq * (V16 ? D * 2 : RB));
   }
   // key block J -> LDS, through the page table for VL
-  constexpr int VRB = DT == kBF16 ? D * 2 : RB;  // bytes per V row in memory
+  constexpr int VRB = V16 ? D * 2 : RB;  // bytes per V row in memory
   auto issue_block = [&](int J, int sub, uint8_t *Kb, uint16_t *Vb) {
     if constexpr (VL) {
       const size_t slab = ((size_t)ptab[J] * hkv + g) * BLK;
@@ -468,7 +470,7 @@ __global__ __launch_bounds__(BLK * 2, (BLK == 64 && D == 128) ? 1 : 2) void attn
   int Jc = ns > 0 ? block_of(0) : -1;
   if (Jc >= 0) {
     issue_block(Jc, 0, Ks0, Vs0);
-    if constexpr (DT == kFP8) T.store_v(Vs0);
+    if constexpr (!V16) T.store_v(Vs0);
   }
   for (int i = 0; i < ns; i += 2) {
 #pragma unroll
@@ -487,7 +489,7 @@ __global__ __launch_bounds__(BLK * 2, (BLK == 64 && D == 128) ? 1 : 2) void attn
         if (Jc >= 0)
           T.compute(ph ? Ks1 : Ks0, ph ? Vs1 : Vs0, Jc * BLK + (ii % NSUB) * KT, Jc == I,
                     DT == kFP8 ? kf : nullptr);
-        if constexpr (DT == kFP8) {
+        if constexpr (!V16) {
           if (Jn >= 0) T.store_v(ph ? Vs0 : Vs1);
         }
         Jc = Jn;
@@ -521,60 +523,69 @@ __global__ __launch_bounds__(BLK * 2, (BLK == 64 && D == 128) ? 1 : 2) void attn
   }
 }
 
-template <int DT, int D, int BLK>
+// kv bytes of one group, for the phase decision: K, and V at its stored width
+template <int DT, int D, bool V16>
+constexpr long kv_row_bytes() {
+  return (long)D * ((DT == kFP8 ? 1 : 2) + (V16 ? 2 : (DT == kFP8 ? 1 : 2)));
+}
+
+template <int DT, int D, int BLK, bool V16>
 static hipError_t launch_t(const Shape &s, const AttnArgs &a, hipStream_t st) {
   const long items = (long)s.hq * s.nb;
-  const int xcd = attn_xcd_mode(s, 2l * s.seq * D * (DT == kFP8 ? 1 : 2));
-  hipLaunchKernelGGL((attn_mfma_kernel<DT, D, BLK, false>), dim3((unsigned)items), dim3(BLK * 2),
-                     0, st, (const uint8_t *)a.q, (const uint8_t *)a.k, (const uint8_t *)a.v,
-                     a.kv_idx, a.kv_cnt, (uint16_t *)a.o, a.lse, a.q_scale, a.k_scale, a.v_scale,
-                     s.hq, s.hkv, s.seq, s.nb, a.sm_scale * kLog2e, xcd, VarlenArgs{});
+  const int xcd = attn_xcd_mode(s, (long)s.seq * kv_row_bytes<DT, D, V16>());
+  hipLaunchKernelGGL((attn_mfma_kernel<DT, D, BLK, false, V16>), dim3((unsigned)items),
+                     dim3(BLK * 2), 0, st, (const uint8_t *)a.q, (const uint8_t *)a.k,
+                     (const uint8_t *)a.v, a.kv_idx, a.kv_cnt, (uint16_t *)a.o, a.lse, a.q_scale,
+                     a.k_scale, a.v_scale, s.hq, s.hkv, s.seq, s.nb, a.sm_scale * kLog2e, xcd,
+                     VarlenArgs{});
   return hipGetLastError();
 }
 
 // Varlen: s.seq = tokens in the packed batch, s.nb = query blocks in it.
-template <int DT, int D, int BLK>
+template <int DT, int D, int BLK, bool V16>
 static hipError_t launch_vl_t(const Shape &s, const AttnArgs &a, const VarlenArgs &v,
                               hipStream_t st) {
   const long items = (long)s.hq * s.nb;
   // a row reads only its own sequence's pages: all groups at once
   const int xcd = attn_xcd_mode(s, 0);
-  hipLaunchKernelGGL((attn_mfma_kernel<DT, D, BLK, true>), dim3((unsigned)items), dim3(BLK * 2),
-                     0, st, (const uint8_t *)a.q, (const uint8_t *)a.k, (const uint8_t *)a.v,
-                     a.kv_idx, a.kv_cnt, (uint16_t *)a.o, a.lse, a.q_scale, a.k_scale, a.v_scale,
-                     s.hq, s.hkv, s.seq, s.nb, a.sm_scale * kLog2e, xcd, v);
+  hipLaunchKernelGGL((attn_mfma_kernel<DT, D, BLK, true, V16>), dim3((unsigned)items),
+                     dim3(BLK * 2), 0, st, (const uint8_t *)a.q, (const uint8_t *)a.k,
+                     (const uint8_t *)a.v, a.kv_idx, a.kv_cnt, (uint16_t *)a.o, a.lse, a.q_scale,
+                     a.k_scale, a.v_scale, s.hq, s.hkv, s.seq, s.nb, a.sm_scale * kLog2e, xcd, v);
   return hipGetLastError();
 }
 
-template <int DT>
+template <int DT, bool V16>
 static hipError_t launch_dt(const Shape &s, const AttnArgs &a, hipStream_t st) {
-  if (s.d == 64 && s.block == 64) return launch_t<DT, 64, 64>(s, a, st);
-  if (s.d == 64 && s.block == 128) return launch_t<DT, 64, 128>(s, a, st);
-  if (s.d == 128 && s.block == 64) return launch_t<DT, 128, 64>(s, a, st);
-  return launch_t<DT, 128, 128>(s, a, st);
+  if (s.d == 64 && s.block == 64) return launch_t<DT, 64, 64, V16>(s, a, st);
+  if (s.d == 64 && s.block == 128) return launch_t<DT, 64, 128, V16>(s, a, st);
+  if (s.d == 128 && s.block == 64) return launch_t<DT, 128, 64, V16>(s, a, st);
+  return launch_t<DT, 128, 128, V16>(s, a, st);
 }
 
-template <int DT>
+template <int DT, bool V16>
 static hipError_t launch_vl_dt(const Shape &s, const AttnArgs &a, const VarlenArgs &v,
                                hipStream_t st) {
-  if (s.d == 64 && s.block == 64) return launch_vl_t<DT, 64, 64>(s, a, v, st);
-  if (s.d == 64 && s.block == 128) return launch_vl_t<DT, 64, 128>(s, a, v, st);
-  if (s.d == 128 && s.block == 64) return launch_vl_t<DT, 128, 64>(s, a, v, st);
-  return launch_vl_t<DT, 128, 128>(s, a, v, st);
+  if (s.d == 64 && s.block == 64) return launch_vl_t<DT, 64, 64, V16>(s, a, v, st);
+  if (s.d == 64 && s.block == 128) return launch_vl_t<DT, 64, 128, V16>(s, a, v, st);
+  if (s.d == 128 && s.block == 64) return launch_vl_t<DT, 128, 64, V16>(s, a, v, st);
+  return launch_vl_t<DT, 128, 128, V16>(s, a, v, st);
 }
 
 hipError_t launch_attn_bf16(const Shape &s, const AttnArgs &a, hipStream_t st) {
-  return launch_dt<kBF16>(s, a, st);
+  return launch_dt<kBF16, true>(s, a, st);
 }
 
 hipError_t launch_attn_fp8(const Shape &s, const AttnArgs &a, hipStream_t st) {
-  return launch_dt<kFP8>(s, a, st);
+  if (s.dtype == kFP8V16) return launch_dt<kFP8, true>(s, a, st);
+  return launch_dt<kFP8, false>(s, a, st);
 }
 
 hipError_t launch_attn_varlen(const Shape &s, const AttnArgs &a, const VarlenArgs &v,
                               hipStream_t st) {
-  if (s.dtype == kBF16) return launch_vl_dt<kBF16>(s, a, v, st);
-  return launch_vl_dt<kFP8>(s, a, v, st);
+  if (s.dtype == kBF16) return launch_vl_dt<kBF16, true>(s, a, v, st);
+  if (s.dtype == kFP8V16) return launch_vl_dt<kFP8, true>(s, a, v, st);
+  return launch_vl_dt<kFP8, false>(s, a, v, st);
 }
 
 }  // namespace bsp

@@ -19,7 +19,8 @@ bsp_status check_desc(const bsp_desc *d, bool need_dtype) {
   if (d->block != 64 && d->block != 128) return BSP_ERR_BAD_SHAPE;
   if (d->causal != 1) return BSP_ERR_UNSUPPORTED;
   if (need_dtype) {
-    if (d->dtype != BSP_DTYPE_F32 && d->dtype != BSP_DTYPE_BF16 && d->dtype != BSP_DTYPE_FP8_E4M3)
+    if (d->dtype != BSP_DTYPE_F32 && d->dtype != BSP_DTYPE_BF16 && d->dtype != BSP_DTYPE_FP8_E4M3 &&
+        d->dtype != BSP_DTYPE_FP8_E4M3_V_BF16)
       return BSP_ERR_BAD_DTYPE;
   }
   if (!isfinite(d->sm_scale)) return BSP_ERR_BAD_VALUE;
@@ -44,6 +45,11 @@ float scale_of(const bsp_desc *d) {
 
 bsp_status hip_status(hipError_t e) { return e == hipSuccess ? BSP_OK : BSP_ERR_HIP; }
 
+// Q and K in e4m3 codes with per-head scales (V's storage aside)
+bool fp8_qk(const bsp_desc *d) {
+  return d->dtype == BSP_DTYPE_FP8_E4M3 || d->dtype == BSP_DTYPE_FP8_E4M3_V_BF16;
+}
+
 }  // namespace
 
 extern "C" {
@@ -54,7 +60,7 @@ bsp_status bsp_score(const bsp_desc *desc, const void *q, const void *k, float *
   if (st != BSP_OK) return st;
   if (desc->seq == 0) return BSP_OK;
   if (!q || !k || !q_pool || !k_pool || !score) return BSP_ERR_NULL_POINTER;
-  const bool fp8 = desc->dtype == BSP_DTYPE_FP8_E4M3;
+  const bool fp8 = fp8_qk(desc);
   if (fp8 && (!desc->q_scale || !desc->k_scale)) return BSP_ERR_BAD_DTYPE;
   if (!fp8 && (desc->q_scale || desc->k_scale || desc->v_scale)) return BSP_ERR_BAD_DTYPE;
   const Shape s = shape_of(desc);
@@ -73,7 +79,7 @@ bsp_status bsp_score_mask(const bsp_desc *desc, const void *q, const void *k, fl
   if (desc->sink_blocks < 0 || desc->local_blocks < 0) return BSP_ERR_BAD_VALUE;
   if (desc->seq == 0) return BSP_OK;
   if (!q || !k || !q_pool || !k_pool || !score || !kv_idx || !kv_cnt) return BSP_ERR_NULL_POINTER;
-  const bool fp8 = desc->dtype == BSP_DTYPE_FP8_E4M3;
+  const bool fp8 = fp8_qk(desc);
   if (fp8 && (!desc->q_scale || !desc->k_scale)) return BSP_ERR_BAD_DTYPE;
   if (!fp8 && (desc->q_scale || desc->k_scale || desc->v_scale)) return BSP_ERR_BAD_DTYPE;
   const Shape s = shape_of(desc);
@@ -90,7 +96,7 @@ bsp_status bsp_score_arith(const bsp_desc *desc, const void *q, const void *k, f
   if (st != BSP_OK) return st;
   if (desc->seq == 0) return BSP_OK;
   if (!q || !k || !k_pool || !score) return BSP_ERR_NULL_POINTER;
-  const bool fp8 = desc->dtype == BSP_DTYPE_FP8_E4M3;
+  const bool fp8 = fp8_qk(desc);
   if (fp8 && (!desc->q_scale || !desc->k_scale)) return BSP_ERR_BAD_DTYPE;
   if (!fp8 && (desc->q_scale || desc->k_scale || desc->v_scale)) return BSP_ERR_BAD_DTYPE;
   Shape s = shape_of(desc);
@@ -122,7 +128,7 @@ bsp_status bsp_score_rescue(const bsp_desc *desc, const void *k, const float *q_
   if (st != BSP_OK) return st;
   if (desc->seq == 0) return BSP_OK;
   if (!k || !q_pool || !k_pool || !k_radius || !rescue) return BSP_ERR_NULL_POINTER;
-  const bool fp8 = desc->dtype == BSP_DTYPE_FP8_E4M3;
+  const bool fp8 = fp8_qk(desc);
   if (fp8 && !desc->k_scale) return BSP_ERR_BAD_DTYPE;
   if (!fp8 && (desc->q_scale || desc->k_scale || desc->v_scale)) return BSP_ERR_BAD_DTYPE;
   const Shape s = shape_of(desc);
@@ -156,7 +162,7 @@ bsp_status bsp_attn_fwd(const bsp_desc *desc, const void *q, const void *k, cons
   if (desc->seq == 0) return BSP_OK;
   if (!q || !k || !v || !o) return BSP_ERR_NULL_POINTER;
   if ((kv_idx == nullptr) != (kv_cnt == nullptr)) return BSP_ERR_NULL_POINTER;
-  const bool fp8 = desc->dtype == BSP_DTYPE_FP8_E4M3;
+  const bool fp8 = fp8_qk(desc);
   if (fp8 && (!desc->q_scale || !desc->k_scale || !desc->v_scale)) return BSP_ERR_BAD_DTYPE;
   if (!fp8 && (desc->q_scale || desc->k_scale || desc->v_scale)) return BSP_ERR_BAD_DTYPE;
   const Shape s = shape_of(desc);
@@ -249,7 +255,7 @@ bsp_status bsp_attn_fwd_varlen(const bsp_desc *desc, const bsp_varlen *vl, const
   if (!vl->cu_seqlens || !vl->cu_blocks || !vl->page_table) return BSP_ERR_NULL_POINTER;
   if (!q || !k_cache || !v_cache || !o) return BSP_ERR_NULL_POINTER;
   if ((kv_idx == nullptr) != (kv_cnt == nullptr)) return BSP_ERR_NULL_POINTER;
-  const bool fp8 = desc->dtype == BSP_DTYPE_FP8_E4M3;
+  const bool fp8 = fp8_qk(desc);
   if (fp8 && (!desc->q_scale || !desc->k_scale || !desc->v_scale)) return BSP_ERR_BAD_DTYPE;
   if (!fp8 && (desc->q_scale || desc->k_scale || desc->v_scale)) return BSP_ERR_BAD_DTYPE;
   Shape s = shape_of(desc);
@@ -295,7 +301,7 @@ bsp_status bsp_score_varlen(const bsp_desc *desc, const bsp_varlen *vl, const vo
   if (empty) return BSP_OK;
   if (!vl->page_table || !q || !k_cache || !q_pool || !k_pool || !score)
     return BSP_ERR_NULL_POINTER;
-  const bool fp8 = desc->dtype == BSP_DTYPE_FP8_E4M3;
+  const bool fp8 = fp8_qk(desc);
   if (fp8 && (!desc->q_scale || !desc->k_scale)) return BSP_ERR_BAD_DTYPE;
   if (!fp8 && (desc->q_scale || desc->k_scale || desc->v_scale)) return BSP_ERR_BAD_DTYPE;
   Shape s = shape_of(desc);
@@ -327,6 +333,16 @@ bsp_status bsp_mask_varlen(const bsp_desc *desc, const bsp_varlen *vl, const flo
   return hip_status(bsp::launch_mask_varlen(s, v, desc->gamma, desc->sink_blocks,
                                             desc->local_blocks, score, user_mask, mask, kv_idx,
                                             kv_cnt, (hipStream_t)stream));
+}
+
+bsp_status bsp_widen_e4m3(const void *src, void *dst, int64_t n, void *stream) {
+  if (n < 0) return BSP_ERR_BAD_SHAPE;
+  if (n == 0) return BSP_OK;
+  if (!src || !dst) return BSP_ERR_NULL_POINTER;
+  if (((uintptr_t)src & 15) || ((uintptr_t)dst & 15)) return BSP_ERR_BAD_VALUE;
+  const uintptr_t s0 = (uintptr_t)src, d0 = (uintptr_t)dst;
+  if (s0 < d0 + 2 * (uintptr_t)n && d0 < s0 + (uintptr_t)n) return BSP_ERR_BAD_VALUE;
+  return hip_status(bsp::launch_widen(src, dst, (long)n, (hipStream_t)stream));
 }
 
 const char *bsp_status_string(int32_t status) {

@@ -19,6 +19,7 @@ constexpr float kLn2 = 0.6931471805599453f;
 constexpr int kF32 = 0;
 constexpr int kBF16 = 1;
 constexpr int kFP8 = 2;
+constexpr int kFP8V16 = 3;  // e4m3 Q and K, V widened to bf16
 
 template <int DT> struct Storage;
 template <> struct Storage<kF32> { static constexpr int bytes = 4; };

@@ -72,6 +72,9 @@ hipError_t launch_attn_f32(const Shape &s, const AttnArgs &a, hipStream_t st);
 hipError_t launch_attn_varlen(const Shape &s, const AttnArgs &a, const VarlenArgs &v,
                               hipStream_t st);
 hipError_t launch_attn_bf16(const Shape &s, const AttnArgs &a, hipStream_t st);
+// e4m3 Q and K; V as e4m3 codes, or bf16 when s.dtype is the mixed code
 hipError_t launch_attn_fp8(const Shape &s, const AttnArgs &a, hipStream_t st);
+// n e4m3 codes -> n bf16 values, exactly
+hipError_t launch_widen(const void *src, void *dst, long n, hipStream_t st);
 
 }  // namespace bsp

@@ -47,7 +47,7 @@
 extern "C" {
 #endif
 
-#define BSP_ABI_VERSION 7
+#define BSP_ABI_VERSION 8
 
 typedef enum bsp_status {
   BSP_OK = 0,
@@ -60,9 +60,15 @@ typedef enum bsp_status {
 } bsp_status;
 
 typedef enum bsp_dtype {
-  BSP_DTYPE_F32 = 0,     /* IEEE binary32 */
-  BSP_DTYPE_BF16 = 1,    /* bfloat16 */
-  BSP_DTYPE_FP8_E4M3 = 2 /* OCP e4m3fn (bias 7, max 448, no inf) times a per-head fp32 scale */
+  BSP_DTYPE_F32 = 0,      /* IEEE binary32 */
+  BSP_DTYPE_BF16 = 1,     /* bfloat16 */
+  BSP_DTYPE_FP8_E4M3 = 2, /* OCP e4m3fn (bias 7, max 448, no inf) times a per-head fp32 scale */
+  /* Q and K as BSP_DTYPE_FP8_E4M3; V in bfloat16 times v_scale[g].  With V
+   * from bsp_widen_e4m3 (exact) the attention result is bit-identical to
+   * BSP_DTYPE_FP8_E4M3 on the codes, and the launch is faster: V tiles then
+   * reach LDS by direct loads instead of being widened in every workgroup.
+   * Entry points that read only Q and K treat it as BSP_DTYPE_FP8_E4M3. */
+  BSP_DTYPE_FP8_E4M3_V_BF16 = 3
 } bsp_dtype;
 
 /* Limits checked by every entry point. */
@@ -221,7 +227,8 @@ bsp_status bsp_mask_dual(const bsp_desc *desc, const float *score, const float *
  * malformed list never reads out of bounds.  The order of a row does not
  * change the result beyond rounding.
  *
- * q, k, v:  device, storage dtype; fp8 needs all three desc scales
+ * q, k, v:  device, storage dtype (v in bfloat16 for BSP_DTYPE_FP8_E4M3_V_BF16);
+ *           the fp8 dtypes need all three desc scales
  * kv_idx, kv_cnt: device, as produced by bsp_mask; both NULL = dense causal
  *           (every J <= I); one NULL and not the other is an error
  * o:        device [hq][seq][d]; float for BSP_DTYPE_F32, bfloat16 otherwise
@@ -295,7 +302,8 @@ typedef struct {
  * sequence end are never read.
  *
  * q:        device [hq][desc->seq][d], storage dtype (bf16 or fp8)
- * k_cache, v_cache: device [pages][hkv][block][d], storage dtype
+ * k_cache, v_cache: device [pages][hkv][block][d], storage dtype (v_cache
+ *           in bfloat16 for BSP_DTYPE_FP8_E4M3_V_BF16)
  * o, lse:   as for bsp_attn_fwd, over the packed tokens
  * fp32 inputs return BSP_ERR_UNSUPPORTED.
  */
@@ -352,6 +360,22 @@ bsp_status bsp_mask_varlen(const bsp_desc *desc, const bsp_varlen *vl, const flo
                            int32_t *kv_cnt, void *stream);
 
 /* Static description of a status code (host, never NULL). */
+/*
+ * bsp_widen_e4m3 - dst[i] = the bfloat16 value of OCP e4m3fn code src[i],
+ * for 0 <= i < n (FP8 inference of the FlashPrefill V2 abstract on the
+ * thelatestinai page: e4m3 operands; the P V product runs on bf16 matrix
+ * cores, so V is widened once here rather than inside every attention
+ * workgroup).  Exact: every e4m3 value is a bf16 value.  Scales are not
+ * applied (V = dst * v_scale[g] as for the codes).
+ *
+ * src:    device, n bytes, 16-byte aligned
+ * dst:    device, n bfloat16 (2n bytes), 16-byte aligned; must not overlap src
+ * n:      >= 0; 0 is a no-op
+ * Errors: BSP_ERR_BAD_SHAPE for n < 0, BSP_ERR_NULL_POINTER, BSP_ERR_BAD_VALUE
+ * for a misaligned or overlapping pair.  Allocates nothing.
+ */
+bsp_status bsp_widen_e4m3(const void *src, void *dst, int64_t n, void *stream);
+
 const char *bsp_status_string(int32_t status);
 
 /* BSP_ABI_VERSION of the loaded library. */

@@ -30,7 +30,7 @@ def test_header_declares_the_entry_points():
     assert _declared() == ["bsp_abi_version", "bsp_attn_fwd", "bsp_attn_fwd_varlen",
                            "bsp_calibrate_gamma", "bsp_mask", "bsp_mask_dual", "bsp_mask_varlen",
                            "bsp_score", "bsp_score_arith", "bsp_score_mask", "bsp_score_rescue",
-                           "bsp_score_varlen", "bsp_status_string"]
+                           "bsp_score_varlen", "bsp_status_string", "bsp_widen_e4m3"]
 
 
 def test_library_exports_every_declared_symbol():
@@ -111,6 +111,31 @@ def test_fp8_scale_rules():
     half.q_scale = 0x2000
     half.k_scale = 0x2000
     assert bsp.bsp_attn_fwd(half, FAKE, FAKE, FAKE, None, None, FAKE, None, None) == 3  # no v_scale
+
+
+def test_mixed_dtype_scale_rules():
+    # e4m3 Q/K with bf16 V: the fp8 scale rules hold, seq == 0 is accepted
+    mix = _d(dtype=bsp.DTYPE_FP8_E4M3_V_BF16)
+    assert bsp.bsp_score(mix, FAKE, FAKE, FAKE, FAKE, FAKE, None) == 3
+    assert bsp.bsp_attn_fwd(mix, FAKE, FAKE, FAKE, None, None, FAKE, None, None) == 3
+    mix.q_scale = mix.k_scale = 0x2000
+    assert bsp.bsp_attn_fwd(mix, FAKE, FAKE, FAKE, None, None, FAKE, None, None) == 3  # no v_scale
+    assert bsp.bsp_attn_fwd(_d(dtype=bsp.DTYPE_FP8_E4M3_V_BF16, seq=0), FAKE, FAKE, FAKE, None,
+                            None, FAKE, None, None) == 0  # a known dtype: empty is a no-op
+    assert bsp.bsp_score(_d(dtype=4), FAKE, FAKE, FAKE, FAKE, FAKE, None) == 3
+
+
+def test_widen_host_checks():
+    w = lambda src, dst, n: bsp.bsp_widen_e4m3(src, dst, n, None)
+    assert w(FAKE, ctypes.c_void_p(0x4000), -1) == 2
+    assert w(None, None, 0) == 0  # n == 0 is a no-op
+    assert w(None, ctypes.c_void_p(0x4000), 16) == 1
+    assert w(FAKE, None, 16) == 1
+    assert w(ctypes.c_void_p(0x1008), ctypes.c_void_p(0x4000), 16) == 4  # misaligned source
+    assert w(FAKE, ctypes.c_void_p(0x4008), 16) == 4  # misaligned destination
+    # overlap: dst covers 2n bytes from 0x1000 - 16
+    assert w(FAKE, ctypes.c_void_p(0x1000 - 16), 16) == 4
+    assert w(ctypes.c_void_p(0x1000 + 32), FAKE, 64) == 4
 
 
 def test_empty_sequence_is_a_no_op():
