@@ -352,34 +352,36 @@ __global__ __launch_bounds__(256, 2) void score_kernel(const float *__restrict__
       if (lane == 0) fz.cnt[(size_t)h * nb + I] = n;
     }
   } else if (vec) {
+    // one wavefront per row, 1 KiB per load instruction, up to 8 in flight
     const int n4 = nb / 4, c4 = jc / 4;
-    constexpr int U = 8;  // loads in flight per thread
-    for (int e0 = threadIdx.x; e0 < rows * n4; e0 += U * NT) {
-      float4 v[U];
+    constexpr int U = 8;
+    for (int rr = w; rr < rows; rr += NWV) {
+      const float M = row_m[rr], inv = row_inv[rr];
+      float4 *prow = (float4 *)(pgrp + (size_t)rr * nb);
+      for (int c0 = lane; c0 < n4; c0 += U * 64) {
+        float4 v[U];
 #pragma unroll
-      for (int k = 0; k < U; ++k) {
-        const int e = e0 + k * NT, rr = e / n4, c = e - rr * n4;
-        v[k] = e < rows * n4 && c < c4 ? *(const float4 *)(pgrp + (size_t)rr * nb + 4 * c)
-                                       : make_float4(-INFINITY, -INFINITY, -INFINITY, -INFINITY);
-      }
+        for (int k = 0; k < U; ++k) {
+          const int c = c0 + k * 64;
+          v[k] = c < c4 ? prow[c] : make_float4(-INFINITY, -INFINITY, -INFINITY, -INFINITY);
+        }
 #pragma unroll
-      for (int k = 0; k < U; ++k) {
-        const int e = e0 + k * NT, rr = e / n4, c = e - rr * n4;
-        if (e < rows * n4) {
-          const float M = row_m[rr], inv = row_inv[rr];
-          *(float4 *)(pgrp + (size_t)rr * nb + 4 * c) =
-              make_float4(__builtin_amdgcn_exp2f(v[k].x - M) * inv,
-                          __builtin_amdgcn_exp2f(v[k].y - M) * inv,
-                          __builtin_amdgcn_exp2f(v[k].z - M) * inv,
-                          __builtin_amdgcn_exp2f(v[k].w - M) * inv);
+        for (int k = 0; k < U; ++k) {
+          const int c = c0 + k * 64;
+          if (c < n4)
+            prow[c] = make_float4(__builtin_amdgcn_exp2f(v[k].x - M) * inv,
+                                  __builtin_amdgcn_exp2f(v[k].y - M) * inv,
+                                  __builtin_amdgcn_exp2f(v[k].z - M) * inv,
+                                  __builtin_amdgcn_exp2f(v[k].w - M) * inv);
         }
       }
     }
   } else {
-    for (int e = threadIdx.x; e < rows * nb; e += NT) {
-      const int rr = e / nb, J = e - rr * nb;
-      float *p = pgrp + (size_t)rr * nb + J;
-      *p = J < jc ? __builtin_amdgcn_exp2f(*p - row_m[rr]) * row_inv[rr] : 0.f;
+    for (int rr = w; rr < rows; rr += NWV) {
+      const float M = row_m[rr], inv = row_inv[rr];
+      float *prow = pgrp + (size_t)rr * nb;
+      for (int J = lane; J < nb; J += 64)
+        prow[J] = J < jc ? __builtin_amdgcn_exp2f(prow[J] - M) * inv : 0.f;
     }
   }
 }
