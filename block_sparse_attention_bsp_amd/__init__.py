@@ -550,10 +550,13 @@ def attn_fwd_varlen(q, k_cache, v_cache, page_table, seqlens, block: int, kv_idx
 
 def prefill_varlen(q, k_cache, v_cache, page_table, seqlens, block: int, gamma: float,
                    sm_scale: float = 0.0, sink_blocks: int = 1, local_blocks: int = 1,
-                   q_scale=None, k_scale=None, v_scale=None):
+                   q_scale=None, k_scale=None, v_scale=None, widen_v: bool = False):
     """All three stages for a packed batch over a paged cache, on the current
-    stream.  Returns a dict of every output."""
+    stream.  Returns a dict of every output.  widen_v: for an e4m3 cache,
+    widen the V cache to bf16 first (every page, used or not; same outputs)."""
     out = {}
+    if widen_v and _is_e4m3(v_cache):
+        v_cache = widen_e4m3(v_cache)
     out["q_pool"], out["k_pool"], out["score"] = score_varlen(
         q, k_cache, page_table, seqlens, block, sm_scale, q_scale, k_scale)
     m, idx, cnt = mask_varlen(out["score"], gamma, seqlens, block, sink_blocks, local_blocks)
