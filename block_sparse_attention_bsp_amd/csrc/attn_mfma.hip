@@ -85,6 +85,17 @@ __device__ __forceinline__ int k_unit(int r, int u) {
   return u ^ ((r / C::KRPW) % C::UNITS);
 }
 
+// e4m3 with d = 128: a read unit is two 16-byte chunks, read by two
+// ds_read_b128 of 16 rows each.  Rows 8-15 of every 16 keep the chunks of a
+// unit in swapped order, so that each read's 16 lanes land on 16 distinct
+// 16-byte bank groups (the unit swizzle alone covers only the even or only
+// the odd ones, and rows r and r + 8 collided).
+template <int DT, int D, int BLK>
+__device__ __forceinline__ int k_half(int r) {
+  using C = AttnCfg<DT, D, BLK>;
+  return C::CPU == 2 ? (r >> 3) & 1 : 0;
+}
+
 // V rows are stored in 16-byte chunks whose index is XORed with a function
 // of the row that moves whole 32-byte pairs, so that the rows one
 // ds_read_b64_tr_b16 reads together (32 bytes from each of 4 rows per 16
@@ -129,6 +140,7 @@ struct Attn {
   uint32_t kdma[KPW / 64], vdma[V16 ? VPW / 64 : 1];
   int krow[KPW / 64], vrow[V16 ? VPW / 64 : 1];
   int koff[DK], voff[NDT];
+  int khalf;  // e4m3, d = 128: byte offset of a unit's first chunk (0 or 16)
   uint4 vreg[V16 ? 1 : VPER];
 
   __device__ __forceinline__ void setup() {
@@ -136,7 +148,7 @@ struct Attn {
     for (int it = 0; it < KPW / 64; ++it) {
       const int p = w * KPW + it * 64 + lane;
       const int r = p / (RB / 16), pc = p % (RB / 16);
-      const int c = k_unit<DT, D, BLK>(r, pc / C::CPU) * C::CPU + pc % C::CPU;
+      const int c = k_unit<DT, D, BLK>(r, pc / C::CPU) * C::CPU + ((pc % C::CPU) ^ k_half<DT, D, BLK>(r));
       kdma[it] = r * RB + c * 16;
       krow[it] = r;
     }
@@ -153,6 +165,7 @@ struct Attn {
 #pragma unroll
     for (int ks = 0; ks < DK; ++ks)
       koff[ks] = r16 * RB + k_unit<DT, D, BLK>(r16, (DT == kFP8 ? 0 : ks * 4) + g) * LB;
+    khalf = k_half<DT, D, BLK>(r16) * 16;
     // V^T (A operand) via ds_read_b64_tr_b16: in lane group g, lane r16 supplies
     // row 4g + r16 / 4 (a key) and columns 4 (r16 % 4) .. + 3 of a 16-wide d
     // tile dt.
@@ -249,7 +262,15 @@ struct Attn {
         const uint4 ab[2] = {lo, make_uint4(0, 0, 0, 0)};
         __builtin_memcpy(&a[kt], ab, 32);
       } else {
-        __builtin_memcpy(&a[kt], Kb + koff[ks] + kt * 16 * RB, sizeof(frag_t));
+        if constexpr (C::CPU == 2) {
+          const uint8_t *u = Kb + koff[ks] + kt * 16 * RB;
+          uint4 h[2];
+          __builtin_memcpy(&h[0], u + khalf, 16);
+          __builtin_memcpy(&h[1], u + (16 - khalf), 16);
+          __builtin_memcpy(&a[kt], h, 32);
+        } else {
+          __builtin_memcpy(&a[kt], Kb + koff[ks] + kt * 16 * RB, sizeof(frag_t));
+        }
       }
     }
   }
