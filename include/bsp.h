@@ -90,7 +90,7 @@ typedef struct bsp_desc {
   int32_t dtype;        /* bsp_dtype of Q, K and V */
   const float *q_scale; /* fp8 only, device [hq]:  Q = code * q_scale[h] */
   const float *k_scale; /* fp8 only, device [hkv]: K = code * k_scale[g] */
-  const float *v_scale; /* fp8 only, device [hkv]: V = code * v_scale[g] */
+  const float *v_scale; /* fp8 only, device [hkv]: V = code (or its bf16 widening) * v_scale[g] */
 } bsp_desc;
 
 /*
