@@ -166,6 +166,30 @@ def test_python_layer_raises_bsp_error():
         bsp.score(x, x, 64)  # host tensors are rejected before the C call
 
 
+def test_binding_picks_the_mixed_dtype_for_a_widened_v():
+    """Host-side dtype selection of the binding (no C call): e4m3 Q/K with a
+    bf16 V is the mixed dtype, with e4m3 V the plain fp8 one; other mixes
+    are rejected."""
+    import torch
+    sc = {}  # the scales are checked in the C call, not in the dtype choice
+    q8 = torch.zeros(4, 256, 128, dtype=torch.uint8)
+    k8 = torch.zeros(2, 256, 128, dtype=torch.uint8)
+    f8 = torch.zeros(2, 256, 128, dtype=torch.float8_e4m3fn)
+    vb = torch.zeros(2, 256, 128, dtype=torch.bfloat16)
+    assert bsp._desc_qkv(q8, k8, 128, v=vb, **sc).dtype == bsp.DTYPE_FP8_E4M3_V_BF16
+    assert bsp._desc_qkv(q8, k8, 128, v=k8, **sc).dtype == bsp.DTYPE_FP8_E4M3
+    assert bsp._desc_qkv(torch.zeros(4, 256, 128, dtype=torch.bfloat16), vb, 128, v=vb).dtype == \
+        bsp.DTYPE_BF16
+    with pytest.raises(bsp.BspError):  # bf16 Q with a bf16 V but e4m3 K
+        bsp._desc_qkv(torch.zeros(4, 256, 128, dtype=torch.bfloat16), k8, 128, v=vb)
+    with pytest.raises(bsp.BspError):  # e4m3 Q/K with an fp32 V
+        bsp._desc_qkv(q8, k8, 128, v=torch.zeros(2, 256, 128), **sc)
+    with pytest.raises(bsp.BspError):  # Q and K must be the same torch type of codes
+        bsp._desc_qkv(q8, f8, 128, v=vb, **sc)
+    with pytest.raises(bsp.BspError):  # widening takes e4m3 codes only
+        bsp.widen_e4m3(vb)
+
+
 def test_calibrate_gamma_host_checks():
     import ctypes as C
     d = bsp.desc(4, 1, 1024, 64, 64, bsp.DTYPE_F32)

@@ -116,3 +116,30 @@ def test_prefill_widens_v_by_default():
     torch.cuda.synchronize()
     for key in ("mask", "kv_cnt", "o", "lse"):
         assert torch.equal(a[key], b[key]), key
+
+
+def test_widen_accepts_torch_float8_codes():
+    """The same bytes as torch.float8_e4m3fn widen to the same bf16 values."""
+    print("\n[case] widen float8_e4m3fn view", flush=True)
+    x = torch.from_numpy(np.random.default_rng(11).integers(0, 256, 4099, dtype=np.uint8)).cuda()
+    a = bsp.widen_e4m3(x)
+    b = bsp.widen_e4m3(x.view(torch.float8_e4m3fn))
+    torch.cuda.synchronize()
+    assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+
+
+def test_prefill_varlen_widen_v_equals_codes():
+    """prefill_varlen with widen_v: every output bit for bit that of the
+    pipeline on the V codes."""
+    lens = [700, 129, 1000, 1]
+    print(f"\n[case] prefill_varlen widen_v lens={lens}", flush=True)
+    from tests.test_parity import _varlen_case
+    c, kc, vc, ptab, _, _ = _varlen_case("fp8", 64, 64, lens, 19, 0.5)
+    dv = H.dev(c)
+    kw = dict(q_scale=dv["q_scale"], k_scale=dv["k_scale"], v_scale=dv["v_scale"])
+    kcd, vcd, pt = (torch.from_numpy(x).cuda() for x in (kc, vc, ptab))
+    a = bsp.prefill_varlen(dv["q"], kcd, vcd, pt, lens, 64, 0.3, **kw)
+    b = bsp.prefill_varlen(dv["q"], kcd, vcd, pt, lens, 64, 0.3, widen_v=True, **kw)
+    torch.cuda.synchronize()
+    for key in ("mask", "kv_cnt", "o", "lse"):
+        assert torch.equal(a[key], b[key]), key
