@@ -2,7 +2,8 @@
 
 One step = the whole hot path on one batch of synthetic input already
 resident in HBM: bsp_score (pool Q/K + block scores), bsp_mask (dynamic
-threshold + index compaction), bsp_attn_fwd (block-sparse attention).
+threshold + index compaction), bsp_attn_fwd (block-sparse attention); for
+e4m3 inputs also bsp_widen_e4m3 of V before the attention launch.
 
 Default workload: a Llama-3-8B-shaped layer at 128K tokens - 32 q / 8 kv
 heads, d = 128, block 128, gamma 0.05, causal, bf16, batch 1 - with the
@@ -11,9 +12,9 @@ seeded RoPE + vertical + slash generator (gen.make_config(3)).
 Prints one JSON line.  value = effective TFLOP/s of the step, i.e. the
 dense-causal FLOPs 4*d*hq*L(L+1)/2 divided by the step time; ms_per_step is
 the ms per layer.  The roofline object describes the attention kernel, the
-dominant one: achieved = kept-block FLOPs per launch / mean launch time
-(HIP events on the stream the kernel runs on) against the dense bf16 MFMA
-peak.  cpu_baseline times the CPU oracle on a bounded row sample of the same
+dominant one: achieved = kept-block FLOPs per launch / median launch time
+over the timed steps (HIP events on the stream the kernel runs on) against
+the dense MFMA peak of the input's dtype.  cpu_baseline times the CPU oracle on a bounded row sample of the same
 layer on the host.
 
 Only one GPU is used: --gpus above 1 exits with a message.
